@@ -1,0 +1,36 @@
+"""Oracle: a plain, slow fp64 CPU definition of Skip-Softmax attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the library calls it: only the tests,
+the smoke check and the benchmark's CPU-baseline leg import it. It shares no
+code with the HIP path; both receive the same inputs from ``synth``.
+
+What it defines (sources: the pages on Skip-Softmax attention):
+
+* ``attention.prefill`` -- FlashAttention-style tiled attention with the
+  Skip-Softmax rule ("TRT-LLM sparse attention" page, the three-step
+  algorithm: block-local max, comparison with the running max, skip of the
+  softmax, the second matmul and the V load; SpargeAttn page, stage two of
+  the online filter, threshold lambda < 0).
+* ``attention.decode`` -- single-token decode with split-K partials and the
+  log-sum-exp combine (same rule; the combine is the standard identity).
+* ``attention.replay`` -- the outputs for a given set of skip decisions.
+* ``block_mask.block_mask`` -- mean-pooled Q/K block scores with top-k,
+  sink block and local window (MInference page, block-sparse pattern and its
+  ``block_sparse_attention(..., topk=64)`` call; NOSA page, section 3:
+  ``init_blocks=1``, ``window_size=1024``, ``topk=64``).
+* ``calibrate.lambda_for_ratio`` -- the threshold that skips a target share
+  of tiles, from the margins.
+* ``bruteforce`` -- a second, scalar-loop implementation for tiny inputs.
+
+Every function is pinned by ``tests/test_oracle_*.py`` against closed forms,
+brute force and invariants.
+"""
+
+from .attention import prefill, decode, replay, combine, visited_tiles, lse_combine_parts
+from .block_mask import pool_blocks, block_scores, block_mask
+from .calibrate import lambda_for_ratio, skip_ratio
+
+__all__ = [
+    "prefill", "decode", "replay", "combine", "visited_tiles", "lse_combine_parts",
+    "pool_blocks", "block_scores", "block_mask", "lambda_for_ratio", "skip_ratio",
+]

@@ -1,0 +1,82 @@
+"""fp64 oracle for the pooled-score block mask (block-sparse prefill).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Definition (MInference page, block-sparse pattern: mean-pool Q and K over
+blocks and use the fact that pooling commutes with the matrix product to
+score whole blocks, then run block-sparse FlashAttention over the chosen
+blocks; its ``block_sparse_attention(q, k, v, topk=64)`` call; NOSA page,
+section 3: keep ``init_blocks=1`` leading block(s) and a ``window_size=1024``
+token local window besides the top-k):
+
+* q_bar[b] = mean of the query rows of block b (``pool`` tokens; the last
+  block may be short), k_bar[c] likewise for keys.
+* score[b, c] = q_bar[b] . k_bar[c] / sqrt(d) for causal candidates c <= b.
+* kept(b) = top-``topk`` candidates by score (ties: lower c first)
+  union {0 .. sink_blocks-1} union {b - W + 1 .. b} with
+  W = ceil(window_tokens / pool), restricted to 0 <= c <= b, listed in
+  ascending order.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .attention import _widen
+
+
+def pool_blocks(x, pool: int, bits: bool = False) -> np.ndarray:
+    """Mean over consecutive blocks of ``pool`` rows along axis -2 (fp64)."""
+    x = _widen(x, bits)
+    L = x.shape[-2]
+    nb = math.ceil(L / pool)
+    out = np.empty(x.shape[:-2] + (nb, x.shape[-1]))
+    for blk in range(nb):
+        out[..., blk, :] = x[..., blk * pool:min(L, (blk + 1) * pool), :].mean(axis=-2)
+    return out
+
+
+def block_scores(q, k, pool: int, bits: bool = False) -> np.ndarray:
+    """Pooled block scores [..., nB, nB] = q_bar k_bar^T / sqrt(d); entries
+    above the diagonal (c > b) are -inf."""
+    qb = pool_blocks(q, pool, bits)
+    kb = pool_blocks(k, pool, bits)
+    d = qb.shape[-1]
+    s = (qb @ np.swapaxes(kb, -1, -2)) / math.sqrt(d)
+    nb = s.shape[-1]
+    s[..., np.triu_indices(nb, 1)[0], np.triu_indices(nb, 1)[1]] = -np.inf
+    return s
+
+
+def block_mask(q, k, pool: int, topk: int, sink_blocks: int, window_tokens: int,
+               bits: bool = False, scores=None) -> dict:
+    """Kept key blocks per query block. q, k [B,H,L,d]. Returns block_idx
+    [B,H,nB,max_blocks] (ascending, padded with -1), block_cnt [B,H,nB],
+    the scores, and the score of the topk-th candidate per row (``kth``),
+    which tests use to locate near-ties."""
+    if scores is None:
+        scores = block_scores(q, k, pool, bits)
+    B, H, nb, _ = scores.shape
+    W = math.ceil(window_tokens / pool) if window_tokens > 0 else 0
+    max_blocks = min(nb, topk + sink_blocks + W)
+    idx = np.full((B, H, nb, max_blocks), -1, np.int64)
+    cnt = np.zeros((B, H, nb), np.int64)
+    kth = np.full((B, H, nb), -np.inf)
+    for b_ in range(B):
+        for h in range(H):
+            for qb in range(nb):
+                cand = scores[b_, h, qb, :qb + 1]
+                order = np.argsort(-cand, kind="stable")
+                top = order[:topk]
+                if len(order) > topk:
+                    kth[b_, h, qb] = cand[order[topk - 1]] if topk > 0 else np.inf
+                keep = set(int(c) for c in top)
+                keep.update(c for c in range(min(sink_blocks, qb + 1)))
+                keep.update(c for c in range(max(0, qb - W + 1), qb + 1))
+                kept = sorted(keep)
+                cnt[b_, h, qb] = len(kept)
+                idx[b_, h, qb, :len(kept)] = kept
+    return {"block_idx": idx, "block_cnt": cnt, "scores": scores, "kth": kth,
+            "max_blocks": max_blocks}

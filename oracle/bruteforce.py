@@ -1,0 +1,133 @@
+"""Scalar-loop second implementation for tiny inputs.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Written with plain Python loops and ``math`` so that it shares no array code
+with ``oracle.attention``; the tests compare the two on many random tiny
+cases. Rule and output as in ``oracle.attention`` (Skip-Softmax three-step
+algorithm of the TRT-LLM page; SpargeAttn stage two).
+"""
+
+from __future__ import annotations
+
+import math
+
+
+def _dot(a, b):
+    t = 0.0
+    for x, y in zip(a, b):
+        t += float(x) * float(y)
+    return t
+
+
+def naive_attention(q, k, v, causal):
+    """softmax(q k^T / sqrt(d)) v for one head: q [Lq][d], k/v [Lk][d]."""
+    d = len(q[0])
+    out, lses = [], []
+    for r, qr in enumerate(q):
+        cols = [c for c in range(len(k)) if (not causal or c <= r)]
+        s = [_dot(qr, k[c]) / math.sqrt(d) for c in cols]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        tot = sum(w)
+        out.append([sum(w[t] * float(v[c][e]) for t, c in enumerate(cols)) / tot
+                    for e in range(len(v[0]))])
+        lses.append(m + math.log(tot))
+    return out, lses
+
+
+def skip_attention(q, k, v, lam, Br, Bc, causal):
+    """One head, prefill. Returns (out, lse, skipped) where skipped is the set
+    of (query tile, key tile) pairs the rule skips."""
+    L, d = len(q), len(q[0])
+    nQ = (L + Br - 1) // Br
+    nK = (L + Bc - 1) // Bc
+    skipped = set()
+    out = [[0.0] * len(v[0]) for _ in range(L)]
+    lses = [-math.inf] * L
+    for i in range(nQ):
+        rows = list(range(i * Br, min(L, (i + 1) * Br)))
+        runmax = {r: -math.inf for r in rows}
+        kept_cols = {r: [] for r in rows}
+        for j in range(nK):
+            cols = list(range(j * Bc, min(L, (j + 1) * Bc)))
+            if causal and cols[0] > rows[-1]:
+                continue
+            worst = -math.inf
+            locs = {}
+            for r in rows:
+                loc = -math.inf
+                for c in cols:
+                    if causal and c > r:
+                        continue
+                    loc = max(loc, _dot(q[r], k[c]) / math.sqrt(d))
+                locs[r] = loc
+                if loc == -math.inf:
+                    gap = -math.inf
+                elif runmax[r] == -math.inf:
+                    gap = math.inf
+                else:
+                    gap = loc - runmax[r]
+                worst = max(worst, gap)
+            skip = worst < lam
+            if skip:
+                skipped.add((i, j))
+            for r in rows:
+                runmax[r] = max(runmax[r], locs[r])
+                if not skip:
+                    kept_cols[r].extend(c for c in cols if not (causal and c > r))
+        for r in rows:
+            cs = kept_cols[r]
+            if not cs:
+                continue
+            s = [_dot(q[r], k[c]) / math.sqrt(d) for c in cs]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            tot = sum(w)
+            out[r] = [sum(w[t] * float(v[c][e]) for t, c in enumerate(cs)) / tot
+                      for e in range(len(v[0]))]
+            lses[r] = m + math.log(tot)
+    return out, lses, skipped
+
+
+def decode_skip_set(q_rows, k, n, lam, Bc, T):
+    """Decode, one KV head: q_rows [G][d], k [n][d]. Skipped tile indices."""
+    d = len(q_rows[0])
+    ntiles = (n + Bc - 1) // Bc
+    skipped = set()
+    for sp in range((ntiles + T - 1) // T):
+        runmax = [-math.inf] * len(q_rows)
+        for j in range(sp * T, min(ntiles, (sp + 1) * T)):
+            worst = -math.inf
+            locs = []
+            for g, qr in enumerate(q_rows):
+                loc = max(_dot(qr, k[c]) / math.sqrt(d) for c in range(j * Bc, min(n, (j + 1) * Bc)))
+                locs.append(loc)
+                gap = math.inf if runmax[g] == -math.inf else loc - runmax[g]
+                worst = max(worst, gap)
+            if worst < lam:
+                skipped.add(j)
+            runmax = [max(a, b) for a, b in zip(runmax, locs)]
+    return skipped
+
+
+def topk_blocks(q, k, pool, topk, sink_blocks, window_tokens):
+    """Block mask for one head by explicit loops: q, k [L][d]."""
+    L, d = len(q), len(q[0])
+    nb = (L + pool - 1) // pool
+
+    def mean(rows):
+        return [sum(float(x[e]) for x in rows) / len(rows) for e in range(d)]
+
+    qb = [mean(q[b * pool:min(L, (b + 1) * pool)]) for b in range(nb)]
+    kb = [mean(k[b * pool:min(L, (b + 1) * pool)]) for b in range(nb)]
+    W = -(-window_tokens // pool) if window_tokens > 0 else 0
+    res = []
+    for b in range(nb):
+        scored = [(-_dot(qb[b], kb[c]) / math.sqrt(d), c) for c in range(b + 1)]
+        scored.sort()
+        keep = {c for _, c in scored[:topk]}
+        keep |= {c for c in range(min(sink_blocks, b + 1))}
+        keep |= {c for c in range(max(0, b - W + 1), b + 1)}
+        res.append(sorted(keep))
+    return res
