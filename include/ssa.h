@@ -1,0 +1,191 @@
+/*
+ * ssa.h -- Skip-Softmax sparse attention for AMD MI355X (gfx950), C ABI.
+ *
+ * The operation (TRT-LLM "Skip Softmax" page, the three-step algorithm;
+ * SpargeAttn page, stage two of the online filter): FlashAttention-style
+ * tiled attention in which, for each query tile and key tile, the kernel
+ * computes S = Q K^T / sqrt(d), takes each row's maximum over the tile
+ * (m_loc) and compares it with the row's running maximum over the tiles
+ * visited before (m_prev). If for EVERY row of the tile m_loc - m_prev is
+ * below lambda (< 0), the tile is skipped: no exponentials, no row-sum
+ * update, no P.V product and no load of the V tile.
+ *
+ *  - gap per row: -inf if the row has no allowed key in the tile, +inf if the
+ *    row has no earlier score (first tile), else m_loc - m_prev; tile margin
+ *    g = max over rows; skip iff g < lambda (strict). lambda <= 0 in natural
+ *    log units of the scaled score; lambda = -INFINITY means dense.
+ *  - key tiles are visited in ascending order (list order with a block list).
+ *  - the output is softmax attention renormalised over the kept tiles;
+ *    lse = ln(sum over kept entries of exp(s)).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers to caller-owned memory; the
+ *    library never allocates or frees device memory and keeps no state.
+ *  - Tensors are dense row-major (innermost dimension contiguous) in the
+ *    layouts given per argument. bf16 = IEEE bfloat16.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    legacy default stream). Outputs are valid once the stream reaches it.
+ *  - Every argument is validated on the host before any HIP call; a failed
+ *    check returns a negative status and enqueues nothing.
+ *  - Thread safety: entry points may be called concurrently from several
+ *    host threads; calls whose output buffers overlap race.
+ */
+#ifndef SSA_H
+#define SSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SSA_OK 0
+#define SSA_ERR_INVALID_ARG (-1) /* null required pointer, bad size, lambda NaN or > 0, ... */
+#define SSA_ERR_UNSUPPORTED (-2) /* valid but not built: head dim, tile sizes, group size */
+#define SSA_ERR_WORKSPACE (-3)   /* workspace null or smaller than the *_workspace_size value */
+#define SSA_ERR_HIP (-4)         /* the HIP runtime reported an error at launch */
+
+/* Values written into the optional per-tile decision arrays. */
+#define SSA_TILE_KEPT 1
+#define SSA_TILE_SKIPPED 2
+
+/*
+ * ssa_prefill -- causal or full Skip-Softmax prefill with grouped-query heads,
+ * optionally restricted to a per-query-tile list of key tiles (block-sparse
+ * prefill: MInference page, block-sparse pattern).
+ *
+ *  q        [B, Hq, L, d]  bf16, required.
+ *  k, v     [B, Hkv, L, d] bf16, required. Query head h reads KV head
+ *           h / (Hq / Hkv).
+ *  out      [B, Hq, L, d]  bf16, required: the renormalised attention output.
+ *  lse      [B, Hq, L]     fp32, nullable: natural-log log-sum-exp of the
+ *           kept scaled scores (-inf for a row with no kept key).
+ *  skip_counts [B, Hq, nQ] int32, nullable: skipped tiles per query tile,
+ *           nQ = ceil(L / Br).
+ *  tile_state  [B, Hq, nQ, nK] uint8, nullable: SSA_TILE_KEPT or
+ *           SSA_TILE_SKIPPED for each visited tile, nK = ceil(L / Bc);
+ *           entries of tiles that are not visited are left untouched.
+ *  tile_margin [B, Hq, nQ, nK] fp32, nullable: the tile margin g (natural
+ *           log units, may be +-inf) of each visited tile; others untouched.
+ *           Margins do not depend on lambda, so one call yields the skip
+ *           ratio of every threshold.
+ *  d in {64, 128}; Br in {64, 128}; Bc = 64. causal: key c is allowed for
+ *  row r iff c <= r (L_q = L_k).
+ *  lambda   <= 0 or -INFINITY; NaN or > 0 is rejected.
+ *  block_idx [B, Hq, nQ, max_blocks] int32, nullable: for query tile i the
+ *           first block_cnt[b,h,i] entries are the key tiles to visit, in
+ *           visit order (ascending expected). Entries < 0, >= nK or above the
+ *           causal limit are ignored. block_cnt [B, Hq, nQ] int32 is required
+ *           with block_idx; counts are clamped to [0, max_blocks].
+ *
+ * Returns SSA_OK or a negative status.
+ */
+int ssa_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
+                int32_t* skip_counts, uint8_t* tile_state, float* tile_margin,
+                int B, int Hq, int Hkv, int L, int d, int Br, int Bc, float lambda,
+                int causal, const int32_t* block_idx, const int32_t* block_cnt,
+                int max_blocks, void* stream);
+
+/*
+ * ssa_decode_workspace_size -- bytes of device workspace ssa_decode needs:
+ * per (sequence, query head, split) one fp32 partial output of d values plus
+ * its running max and row-sum. Returns 0 for invalid sizes.
+ */
+size_t ssa_decode_workspace_size(int B, int Hq, int S_max, int d, int Bc, int split_tiles);
+
+/*
+ * ssa_decode -- one new query token per sequence against a KV cache, split-K
+ * over the cache with a log-sum-exp combine (TRT-LLM Skip Softmax page: the
+ * decode phase is memory-bound and the skip avoids loading V tiles).
+ *
+ *  q        [B, Hq, d] bf16, required.
+ *  k_cache, v_cache [B, Hkv, S_max, d] bf16, required; rows [0, seqlens[b])
+ *           of sequence b are valid and no other row is read.
+ *  seqlens  [B] int32 device array, required; each value is clamped to
+ *           [0, S_max]. A length of 0 gives out = 0 and lse = -inf.
+ *  out      [B, Hq, d] bf16, required.  lse [B, Hq] fp32, nullable.
+ *  skip_counts [B, Hkv, nS] int32, nullable, nS = ceil(ceil(S_max/Bc) /
+ *           split_tiles): skipped tiles per split (0 for splits past the end).
+ *  tile_state, tile_margin [B, Hkv, nT] uint8 / fp32, nullable,
+ *           nT = ceil(S_max / Bc): per visited key tile, as in ssa_prefill.
+ *  The decision unit is (sequence, KV head, split): the G = Hq/Hkv query
+ *  heads sharing a KV head form the rows of a tile, so a V tile is loaded
+ *  unless every one of them can skip it. Each split of split_tiles key tiles
+ *  restarts the running max, so its first tile is always kept.
+ *  d in {64, 128}; Bc = 64; G in {1, 2, 4, 8, 16}; split_tiles >= 1.
+ *  workspace: device buffer of at least ssa_decode_workspace_size(...) bytes,
+ *           4-byte aligned; its contents on entry are ignored.
+ */
+int ssa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
+               void* out, float* lse, int32_t* skip_counts, uint8_t* tile_state,
+               float* tile_margin, int B, int Hq, int Hkv, int S_max, int d, int Bc,
+               int split_tiles, float lambda, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/*
+ * ssa_block_mask_max_blocks -- length of the kept-block list per query block
+ * that ssa_block_mask can produce: min(nB, topk + sink_blocks + W) with
+ * nB = ceil(L / pool) and W = ceil(window_tokens / pool). Returns -1 for
+ * invalid sizes.
+ */
+int ssa_block_mask_max_blocks(int L, int pool, int topk, int sink_blocks, int window_tokens);
+
+/*
+ * ssa_block_mask_workspace_size -- bytes of device workspace ssa_block_mask
+ * needs (the pooled Q and K, fp32 [B, H, nB, d] each).
+ */
+size_t ssa_block_mask_workspace_size(int B, int H, int L, int d, int pool);
+
+/*
+ * ssa_block_mask -- predicted block-sparse mask from mean-pooled Q and K
+ * (MInference page, block-sparse pattern: mean pooling commutes with the
+ * matrix product, so pooled scores estimate block importance; its
+ * block_sparse_attention(q, k, v, topk=64); NOSA page, section 3: always keep
+ * init_blocks leading block(s) and a local window of window_size tokens).
+ *
+ *  q, k     [B, H, L, d] bf16, required (one KV head per query head).
+ *  For query block b (pool tokens): q_bar, k_bar = fp32 means over the rows
+ *  of each block (the last block may be short); score(b, c) =
+ *  q_bar[b] . k_bar[c] / sqrt(d) for c <= b. Kept: the topk highest-scoring
+ *  candidates (ties: lower c first), plus blocks 0..sink_blocks-1, plus
+ *  blocks b-W+1..b with W = ceil(window_tokens / pool), all within [0, b].
+ *  block_idx [B, H, nB, max_blocks] int32, required: kept blocks in
+ *           ascending order, padded with -1. max_blocks must be at least
+ *           ssa_block_mask_max_blocks(...).
+ *  block_cnt [B, H, nB] int32, required: number of kept blocks.
+ *  block_scores [B, H, nB, nB] fp32, nullable: the pooled scores (entries
+ *           above the diagonal are -inf).
+ *  Only causal masks are built (causal must be 1). d in {64, 128};
+ *  pool = 64; nB <= 4096. The result feeds ssa_prefill with Br = Bc = pool.
+ *  workspace: at least ssa_block_mask_workspace_size(...) bytes, 16-byte
+ *           aligned.
+ */
+int ssa_block_mask(const void* q, const void* k, int B, int H, int L, int d, int pool,
+                   int topk, int sink_blocks, int window_tokens, int causal,
+                   int32_t* block_idx, int32_t* block_cnt, int max_blocks,
+                   float* block_scores, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
+ * ssa_lambda_from_scale_factor -- threshold from a context-length scale
+ * factor (TRT-LLM page: the configured threshold_scale_factor is divided by
+ * the context length to give the actual threshold, so longer contexts skip
+ * more). Read here as a threshold on the softmax value ratio
+ * exp(m_loc - m_prev) < scale_factor / L, i.e. lambda = ln(scale_factor / L),
+ * clamped to <= 0. Returns NaN for scale_factor <= 0 or L <= 0.
+ */
+float ssa_lambda_from_scale_factor(float scale_factor, int L);
+
+/* Human-readable name of a status code (static string). */
+const char* ssa_status_string(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+int ssa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSA_H */

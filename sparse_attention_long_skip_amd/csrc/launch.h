@@ -1,0 +1,75 @@
+// Host-side launch interface between the C ABI (ssa_api.cpp) and the kernels.
+// Arguments reaching these functions have already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssa {
+
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  int32_t* skip_counts;
+  uint8_t* tile_state;
+  float* tile_margin;
+  int B, Hq, Hkv, L, d, Br, Bc;
+  float lambda;
+  int causal;
+  const int32_t* block_idx;
+  const int32_t* block_cnt;
+  int max_blocks;
+};
+
+struct DecodeParams {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* seqlens;
+  void* out;
+  float* lse;
+  int32_t* skip_counts;
+  uint8_t* tile_state;
+  float* tile_margin;
+  int B, Hq, Hkv, S_max, d, Bc, split_tiles;
+  float lambda;
+  void* workspace;
+};
+
+struct MaskParams {
+  const void* q;
+  const void* k;
+  int B, H, L, d, pool, topk, sink_blocks, window_tokens;
+  int32_t* block_idx;
+  int32_t* block_cnt;
+  int max_blocks;
+  float* block_scores;
+  void* workspace;
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_block_mask(const MaskParams& p, hipStream_t stream);
+
+// Decode workspace layout: partial o [B, Hq, nS, d] fp32, then (m, l) [B, Hq, nS, 2] fp32.
+inline size_t decode_num_splits(int S_max, int Bc, int split_tiles) {
+  size_t nT = ((size_t)S_max + Bc - 1) / Bc;
+  return (nT + split_tiles - 1) / split_tiles;
+}
+
+inline size_t decode_workspace_bytes(int B, int Hq, int S_max, int d, int Bc, int split_tiles) {
+  size_t nS = decode_num_splits(S_max, Bc, split_tiles);
+  return (size_t)B * Hq * nS * ((size_t)d + 2) * sizeof(float);
+}
+
+inline size_t mask_workspace_bytes(int B, int H, int L, int d, int pool) {
+  size_t nB = ((size_t)L + pool - 1) / pool;
+  return 2 * (size_t)B * H * nB * d * sizeof(float);
+}
+
+}  // namespace ssa

@@ -1,0 +1,356 @@
+// Skip-Softmax prefill kernel for gfx950.
+//
+// Operation (TRT-LLM "Skip Softmax" page, three-step algorithm; SpargeAttn
+// page, stage two): FlashAttention tiled attention; per (query tile, key
+// tile) the tile is skipped -- no exp, no P.V, no V load -- when every row's
+// block-local max is more than |lambda| below its running max.
+//
+// Design:
+//  * One workgroup per (batch, query head, query tile of BR rows); BR/32
+//    waves, each owning 32 query rows. Heavy (late, causal) tiles launch
+//    first.
+//  * Scores are computed transposed, S^T = K Q^T, with 32x32x16 bf16 MFMA:
+//    K rows come from LDS (A operand), Q stays in registers (B operand). The
+//    accumulator then gives every lane ONE query row (lane % 32) and 16 keys
+//    per 32-key block, so row max / row sum / rescale are lane-local plus one
+//    exchange between the two half-waves.
+//  * The output is accumulated transposed as well, O^T = V^T P^T: the P
+//    registers are already the B operand (same lane = query), and V is
+//    written to LDS transposed (d-major) so the A operand is two 8-byte LDS
+//    reads per lane.
+//  * K tiles are double-buffered in LDS and prefetched one tile ahead into
+//    registers. The vote: each wave reduces its rows' gaps to a max; the
+//    workgroup max decides, uniformly, whether the tile is skipped. Only then
+//    are the V loads issued, and the exp / rescale work overlaps them.
+#include "common.h"
+#include "launch.h"
+
+namespace ssa {
+
+namespace {
+
+constexpr int BC = 64;
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;
+  float* lse;
+  int32_t* skip_counts;
+  uint8_t* tile_state;
+  float* tile_margin;
+  int B, Hq, Hkv, L, nQ, nK, G;
+  float lam_raw;     // lambda * sqrt(d): threshold on raw q.k differences
+  float c_log2;      // log2(e) / sqrt(d)
+  float inv_sqrt_d;
+  int causal;
+  const int32_t* block_idx;
+  const int32_t* block_cnt;
+  int max_blocks;
+};
+
+template <int D, int BR>
+__global__ __launch_bounds__(BR * 2) void prefill_kernel(PrefillArgs a) {
+  constexpr int NW = BR / 32;
+  constexpr int NT = NW * kWave;
+  constexpr int KP = D + 8;   // K tile row pitch in LDS (bf16 elements)
+  constexpr int VP = BC + 4;  // transposed V row pitch in LDS (bf16 elements)
+  constexpr int NKK = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int KCH = BC * D / 8 / NT;         // 16-byte K chunks per thread
+  constexpr int NVG = 16 * (D / 8);            // (4 keys x 8 d) V groups per tile
+  constexpr int VCH = (NVG + NT - 1) / NT;
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BC * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VP];
+  __shared__ float gap_lds[2][NW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+
+  int bid = blockIdx.x;
+  const int hq = bid % a.Hq;
+  bid /= a.Hq;
+  const int i = a.nQ - 1 - (bid % a.nQ);
+  const int b = bid / a.nQ;
+  const int kvh = hq / a.G;
+  const int L = a.L;
+  const int q0 = i * BR;
+  const int row = q0 + w * 32 + r32;
+  const bool row_ok = row < L;
+  const int last_row = min(q0 + BR, L) - 1;
+
+  const uint16_t* qp = a.q + ((size_t)(b * a.Hq + hq) * L) * D;
+  const uint16_t* kp = a.k + ((size_t)(b * a.Hkv + kvh) * L) * D;
+  const uint16_t* vp = a.v + ((size_t)(b * a.Hkv + kvh) * L) * D;
+  const size_t unit = ((size_t)(b * a.Hq + hq) * a.nQ + i);
+
+  // Query rows as the B operand: lane holds row (lane % 32), d chunk 16*kk + 8h.
+  bf16x8 qf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (row_ok) x = load16(qp + (size_t)row * D + kk * 16 + h * 8);
+    qf[kk] = as_bf16x8(x);
+  }
+
+  // Visit list: dense (ascending tiles up to the causal limit) or a block list.
+  const int32_t* list = nullptr;
+  int n_list;
+  if (a.block_idx) {
+    list = a.block_idx + unit * a.max_blocks;
+    n_list = min(max(a.block_cnt[unit], 0), a.max_blocks);
+  } else {
+    n_list = a.causal ? (last_row / BC + 1) : a.nK;
+  }
+  auto tile_of = [&](int t) -> int { return list ? list[t] : t; };
+  auto valid = [&](int j) -> bool {
+    return j >= 0 && j < a.nK && (!a.causal || j * BC <= last_row);
+  };
+  auto next_valid = [&](int t) -> int {
+    if (!list) return t;
+    while (t < n_list && !valid(list[t])) ++t;
+    return t;
+  };
+
+  u32x4 kreg[KCH];
+  auto load_k = [&](int j) {
+#pragma unroll
+    for (int r = 0; r < KCH; ++r) {
+      const int id = tid + NT * r;
+      const int key = j * BC + id / (D / 8);
+      const int c = id % (D / 8);
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (key < L) x = load16(kp + (size_t)key * D + c * 8);
+      kreg[r] = x;
+    }
+  };
+  auto store_k = [&](uint16_t* dst) {
+#pragma unroll
+    for (int r = 0; r < KCH; ++r) {
+      const int id = tid + NT * r;
+      store16(dst + (id / (D / 8)) * KP + (id % (D / 8)) * 8, kreg[r]);
+    }
+  };
+
+  float m_prev = -INFINITY;  // running max of raw q.k for this lane's row
+  float l_acc = 0.f;         // partial row sum over this lane's keys
+  f32x16 o[NDB];
+#pragma unroll
+  for (int nb = 0; nb < NDB; ++nb)
+    for (int e = 0; e < 16; ++e) o[nb][e] = 0.f;
+  int skipped = 0;
+
+  int t = next_valid(0);
+  if (t < n_list) load_k(tile_of(t));
+  int it = 0;
+  while (t < n_list) {
+    const int j = tile_of(t);
+    const int tn = next_valid(t + 1);
+    const int buf = it & 1;
+    uint16_t* kl = k_lds[buf];
+    store_k(kl);
+    __syncthreads();
+    if (tn < n_list) load_k(tile_of(tn));
+
+    // S^T = K Q^T for this wave's 32 rows and the tile's 64 keys.
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        bf16x8 ka = as_bf16x8(load16(kl + (kb * 32 + r32) * KP + kk * 16 + h * 8));
+        s[kb] = mfma32(ka, qf[kk], s[kb]);
+      }
+    }
+    const int kbase = j * BC;
+    const bool need_mask = (kbase + BC > L) || (a.causal && kbase + BC - 1 > q0 + w * 32);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kbase + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
+          if (key >= L || (a.causal && key > row)) s[kb][e] = -INFINITY;
+        }
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, s[kb][e]);
+    mloc = fmaxf(mloc, swap_halves(mloc));
+    float gap;
+    if (!row_ok || mloc == -INFINITY) gap = -INFINITY;
+    else if (m_prev == -INFINITY) gap = INFINITY;
+    else gap = mloc - m_prev;
+    gap = wave_max(gap);
+    if (lane == 0) gap_lds[buf][w] = gap;
+    __syncthreads();
+    float g = gap_lds[buf][0];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) g = fmaxf(g, gap_lds[buf][ww]);
+    const bool skip = g < a.lam_raw;
+    if (tid == 0) {
+      const size_t ti = unit * a.nK + j;
+      if (a.tile_state) a.tile_state[ti] = skip ? 2 : 1;
+      if (a.tile_margin) a.tile_margin[ti] = g * a.inv_sqrt_d;
+    }
+
+    if (!skip) {
+      // V loads for this tile: 4 consecutive keys x 8 d per group.
+      u32x4 vreg[VCH][4];
+#pragma unroll
+      for (int r = 0; r < VCH; ++r) {
+        const int id = tid + NT * r;
+        const int g4 = id & 15;
+        const int c = id >> 4;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int key = kbase + 4 * g4 + rr;
+          u32x4 x = {0u, 0u, 0u, 0u};
+          if ((NVG % NT == 0 || id < NVG) && key < L) x = load16(vp + (size_t)key * D + c * 8);
+          vreg[r][rr] = x;
+        }
+      }
+      // Online softmax update (exp2 with the 1/sqrt(d) and log2(e) folded in).
+      const float m_new = fmaxf(m_prev, mloc);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2((m_prev - m_use) * a.c_log2);
+      const float mc = m_use * a.c_log2;
+      bf16x8 p[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float x0 = fast_exp2(fmaf(s[kb][gp * 8 + e], a.c_log2, -mc));
+            const float x1 = fast_exp2(fmaf(s[kb][gp * 8 + e + 1], a.c_log2, -mc));
+            psum += x0 + x1;
+            pk[e >> 1] = pack_bf16x2(x0, x1);
+          }
+          p[kb * 2 + gp] = as_bf16x8(pk);
+        }
+      l_acc = l_acc * alpha + psum;
+#pragma unroll
+      for (int nb = 0; nb < NDB; ++nb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[nb][e] *= alpha;
+      m_prev = m_new;
+
+      // V tile -> LDS, transposed to [d][key].
+#pragma unroll
+      for (int r = 0; r < VCH; ++r) {
+        const int id = tid + NT * r;
+        if (NVG % NT == 0 || id < NVG) {
+          const int g4 = id & 15;
+          const int c = id >> 4;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t a0 = vreg[r][0][m], a1 = vreg[r][1][m], a2 = vreg[r][2][m], a3 = vreg[r][3][m];
+            u32x2 lo, hi;
+            lo[0] = (a0 & 0xffffu) | (a1 << 16);
+            lo[1] = (a2 & 0xffffu) | (a3 << 16);
+            hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
+            hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+            *reinterpret_cast<u32x2*>(vt_lds + (c * 8 + 2 * m) * VP + 4 * g4) = lo;
+            *reinterpret_cast<u32x2*>(vt_lds + (c * 8 + 2 * m + 1) * VP + 4 * g4) = hi;
+          }
+        }
+      }
+      __syncthreads();
+      // O^T += V^T P^T
+#pragma unroll
+      for (int nb = 0; nb < NDB; ++nb) {
+        const uint16_t* vrow = vt_lds + (nb * 32 + r32) * VP + h * 4;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int gp = 0; gp < 2; ++gp) {
+            const int kc = kb * 32 + gp * 16;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kc);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + kc + 8);
+            u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+            o[nb] = mfma32(as_bf16x8(va), p[kb * 2 + gp], o[nb]);
+          }
+      }
+    } else {
+      ++skipped;
+      m_prev = fmaxf(m_prev, mloc);
+    }
+    t = tn;
+    ++it;
+  }
+
+  // Epilogue: normalise, write out (bf16) and lse.
+  const float l_tot = l_acc + swap_halves(l_acc);
+  if (row_ok) {
+    const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* op = a.out + ((size_t)(b * a.Hq + hq) * L + row) * D;
+#pragma unroll
+    for (int nb = 0; nb < NDB; ++nb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        u32x2 st;
+        st[0] = pack_bf16x2(o[nb][g4 * 4 + 0] * inv_l, o[nb][g4 * 4 + 1] * inv_l);
+        st[1] = pack_bf16x2(o[nb][g4 * 4 + 2] * inv_l, o[nb][g4 * 4 + 3] * inv_l);
+        *reinterpret_cast<u32x2*>(op + nb * 32 + g4 * 8 + h * 4) = st;
+      }
+    if (a.lse && h == 0)
+      a.lse[(size_t)(b * a.Hq + hq) * L + row] =
+          l_tot > 0.f ? m_prev * a.inv_sqrt_d + __logf(l_tot) : -INFINITY;
+  }
+  if (a.skip_counts && tid == 0) a.skip_counts[unit] = skipped;
+}
+
+template <int D, int BR>
+hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)((size_t)a.B * a.Hq * a.nQ));
+  dim3 block(BR * 2);
+  hipLaunchKernelGGL((prefill_kernel<D, BR>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+  PrefillArgs a;
+  a.q = static_cast<const uint16_t*>(p.q);
+  a.k = static_cast<const uint16_t*>(p.k);
+  a.v = static_cast<const uint16_t*>(p.v);
+  a.out = static_cast<uint16_t*>(p.out);
+  a.lse = p.lse;
+  a.skip_counts = p.skip_counts;
+  a.tile_state = p.tile_state;
+  a.tile_margin = p.tile_margin;
+  a.B = p.B;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.L = p.L;
+  a.nQ = (p.L + p.Br - 1) / p.Br;
+  a.nK = (p.L + p.Bc - 1) / p.Bc;
+  a.G = p.Hq / p.Hkv;
+  const float sd = sqrtf((float)p.d);
+  a.lam_raw = p.lambda * sd;
+  a.c_log2 = kLog2e / sd;
+  a.inv_sqrt_d = 1.f / sd;
+  a.causal = p.causal;
+  a.block_idx = p.block_idx;
+  a.block_cnt = p.block_cnt;
+  a.max_blocks = p.max_blocks;
+  if (p.d == 128 && p.Br == 128) return launch<128, 128>(a, stream);
+  if (p.d == 128 && p.Br == 64) return launch<128, 64>(a, stream);
+  if (p.d == 64 && p.Br == 128) return launch<64, 128>(a, stream);
+  if (p.d == 64 && p.Br == 64) return launch<64, 64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ssa

@@ -1,0 +1,129 @@
+"""Shared helpers for the GPU parity tests: move generator outputs to the
+device and compare the HIP path with the oracle.
+
+Acceptance (applies to every parity test):
+* outputs: max |gpu - oracle| <= 2e-2 and ||gpu - oracle||_2 / ||oracle||_2 <= 1e-2;
+  lse: max abs <= 2e-2 (bf16 inputs, fp32 accumulation, P rounded to bf16 for
+  the second product on the GPU; fp64 in the oracle).
+* the set of visited tiles matches exactly; skip decisions match exactly
+  except for tiles whose oracle margin lies within BAND of lambda (the GPU
+  takes the decision on fp32 scores, the oracle on fp64). Such tiles are
+  counted; units that contain one are compared against the oracle's replay
+  of the GPU's own decisions.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from oracle.attention import KEPT, SKIPPED, NOT_VISITED
+
+ATOL = 2e-2
+RTOL_L2 = 1e-2
+BAND = 1e-3
+
+
+def dev_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy()
+
+
+def assert_close(name, got, ref, atol=ATOL, rtol_l2=RTOL_L2):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin), f"{name}: finiteness differs"
+    if not fin.any():
+        return 0.0, 0.0
+    err = np.abs(got[fin] - ref[fin])
+    mx = float(err.max())
+    nrm = float(np.linalg.norm(ref[fin]))
+    rel = float(np.linalg.norm(got[fin] - ref[fin]) / nrm) if nrm > 0 else mx
+    assert mx <= atol, f"{name}: max abs err {mx:.3e} > {atol}"
+    assert rel <= rtol_l2 or nrm == 0, f"{name}: rel L2 err {rel:.3e} > {rtol_l2}"
+    return mx, rel
+
+
+def compare_decisions(gpu_state, ref_decision, ref_margin, lam, band=BAND):
+    """Exact match of visited sets and of decisions outside the band.
+    Returns (n_exempt_disagreements, mask of tiles that disagree)."""
+    gpu_state = np.asarray(gpu_state)
+    ref_decision = np.asarray(ref_decision)
+    vis_g = gpu_state != NOT_VISITED
+    vis_r = ref_decision != NOT_VISITED
+    assert np.array_equal(vis_g, vis_r), f"visited sets differ at {np.argwhere(vis_g != vis_r)[:5]}"
+    diff = vis_r & (gpu_state != ref_decision)
+    if diff.any():
+        near = np.abs(ref_margin - lam) < band
+        bad = diff & ~near
+        assert not bad.any(), (
+            f"{int(bad.sum())} skip decisions differ outside the band; first at "
+            f"{np.argwhere(bad)[:3].tolist()} margins {ref_margin[bad][:3]}")
+    return int(diff.sum()), diff
+
+
+def prefill_parity(q_bits, k_bits, v_bits, lam, Br, Bc, causal, block_idx=None, block_cnt=None,
+                   units=None, margins_atol=1e-3):
+    """Run the HIP prefill on the whole input and the oracle on ``units``
+    (all if None); compare. Returns a summary dict."""
+    import sparse_attention_long_skip_amd as ssa
+    q, k, v = dev_bf16(q_bits), dev_bf16(k_bits), dev_bf16(v_bits)
+    bi = bc = None
+    if block_idx is not None:
+        bi = torch.from_numpy(np.ascontiguousarray(block_idx, np.int32)).cuda()
+        bc = torch.from_numpy(np.ascontiguousarray(block_cnt, np.int32)).cuda()
+    g = ssa.prefill(q, k, v, lam, Br=Br, Bc=Bc, causal=causal, block_idx=bi, block_cnt=bc,
+                    lse=True, stats=True, margins=True)
+    torch.cuda.synchronize()
+    ref = oracle.prefill(q_bits, k_bits, v_bits, lam, Br, Bc, causal, block_idx=block_idx,
+                         block_cnt=block_cnt, units=units, bits=True)
+    state = to_np(g["tile_state"])
+    margin = to_np(g["tile_margin"])
+    B, Hq, L, d = q_bits.shape
+    if units is None:
+        units = [(b, h, i) for b in range(B) for h in range(Hq) for i in range(state.shape[2])]
+    sel = tuple(np.array(units).T)
+    n_exempt, diff = compare_decisions(state[sel], ref["decision"][sel], ref["margin"][sel], lam)
+    # margins: same visited set, close values
+    rm, gm = ref["margin"][sel], margin[sel]
+    vis = ref["decision"][sel] != NOT_VISITED
+    assert np.array_equal(np.isposinf(gm[vis]), np.isposinf(rm[vis]))
+    assert np.array_equal(np.isneginf(gm[vis]), np.isneginf(rm[vis]))
+    fin = vis & np.isfinite(rm)
+    if fin.any():
+        assert np.max(np.abs(gm[fin] - rm[fin])) < margins_atol
+    # skip counts
+    sc = to_np(g["skip_counts"])[sel]
+    assert np.array_equal(sc, (state[sel] == SKIPPED).sum(axis=-1))
+    # outputs, unit by unit rows
+    out_g = to_np(g["out"])
+    lse_g = to_np(g["lse"])
+    replay_units = [u for u, dd in zip(units, diff.any(axis=-1)) if dd]
+    rep = None
+    if replay_units:
+        forced = state.astype(np.int8)
+        rep = oracle.replay(q_bits, k_bits, v_bits, forced, Br, Bc, causal, block_idx=block_idx,
+                            block_cnt=block_cnt, units=replay_units, bits=True)
+    got_o, ref_o, got_l, ref_l = [], [], [], []
+    rs = set(replay_units)
+    for (b, h, i) in units:
+        r0, r1 = i * Br, min(L, (i + 1) * Br)
+        src = rep if (b, h, i) in rs else ref
+        got_o.append(out_g[b, h, r0:r1])
+        ref_o.append(src["out"][b, h, r0:r1])
+        got_l.append(lse_g[b, h, r0:r1])
+        ref_l.append(src["lse"][b, h, r0:r1])
+    mo = assert_close("out", np.concatenate(got_o), np.concatenate(ref_o))
+    ml = assert_close("lse", np.concatenate(got_l), np.concatenate(ref_l), rtol_l2=1.0)
+    n_vis = int(vis.sum())
+    n_skip = int((state[sel] == SKIPPED).sum())
+    return {"max_err_out": mo[0], "rel_l2_out": mo[1], "max_err_lse": ml[0], "exempt": n_exempt,
+            "visited": n_vis, "skipped": n_skip, "gpu": g, "ref": ref}

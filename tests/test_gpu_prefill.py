@@ -1,0 +1,84 @@
+"""GPU parity: Skip-Softmax prefill (HIP, through the C ABI) against the oracle."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import prefill_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(cfg, seed, B, Hq, Hkv, L, d, frac=0.1):
+    x = synth.prefill_inputs(cfg, seed, B, Hq, Hkv, L, d, block=64, frac=frac)
+    return x["q"], x["k"], x["v"]
+
+
+@pytest.mark.parametrize("d,Br", [(64, 64), (128, 128), (128, 64), (64, 128)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_dense_small_ragged(d, Br, causal):
+    # L = 333 spans several tiles of both sizes with a ragged tail.
+    q, k, v = _inputs(200, 1, 1, 2, 1, 333, d)
+    r = prefill_parity(q, k, v, -math.inf, Br, 64, causal)
+    print(f"d={d} Br={Br} causal={causal}: max err {r['max_err_out']:.2e} rel {r['rel_l2_out']:.2e}")
+    assert r["skipped"] == 0
+
+
+@pytest.mark.parametrize("d,Br", [(64, 64), (128, 128)])
+def test_skip_small_gqa(d, Br):
+    q, k, v = _inputs(201, 2, 2, 8, 2, 1000, d)
+    B, Hq, L, _ = q.shape
+    m = oracle.prefill(q, k, v, -math.inf, Br, 64, True, bits=True)["margin"]
+    lam = oracle.lambda_for_ratio(m, 0.5)
+    r = prefill_parity(q, k, v, lam, Br, 64, True)
+    print(f"lam={lam:.4f} skipped {r['skipped']}/{r['visited']} exempt {r['exempt']} "
+          f"err {r['max_err_out']:.2e}")
+    # at this length half the margins are positive, so lambda clamps to 0;
+    # a fifth of the tiles still skip
+    assert r["skipped"] > 0.05 * r["visited"]
+
+
+def test_config0_full():
+    c = synth.CONFIGS[0]
+    q, k, v = _inputs(0, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], c["frac"])
+    r = prefill_parity(q, k, v, c["lam"], c["Br"], c["Bc"], c["causal"])
+    print(f"config 0: skipped {r['skipped']}/{r['visited']} err {r['max_err_out']:.2e}")
+
+
+def test_single_row_and_tiny():
+    for L in (1, 2, 63, 65):
+        q, k, v = _inputs(202, L, 1, 1, 1, L, 64)
+        prefill_parity(q, k, v, -2.0, 64, 64, True)
+
+
+def test_block_list_prefill_small():
+    q, k, v = _inputs(203, 0, 1, 2, 2, 700, 64)
+    nQ = math.ceil(700 / 64)
+    rng = np.random.default_rng(0)
+    idx = np.full((1, 2, nQ, 8), -1, np.int32)
+    cnt = np.zeros((1, 2, nQ), np.int32)
+    for h in range(2):
+        for i in range(nQ):
+            keep = sorted(set(rng.choice(i + 1, size=min(i + 1, 5), replace=False).tolist()) | {i})[:8]
+            idx[0, h, i, :len(keep)] = keep
+            cnt[0, h, i] = len(keep)
+    # an invalid entry (above the causal limit) is ignored
+    idx[0, 0, 0, 1] = 5
+    cnt[0, 0, 0] = 2
+    for lam in (-math.inf, -1.0):
+        prefill_parity(q, k, v, lam, 64, 64, True, block_idx=idx, block_cnt=cnt)
+
+
+def test_deterministic_repeat():
+    import torch
+    import sparse_attention_long_skip_amd as ssa
+    from parity import dev_bf16
+    q, k, v = _inputs(204, 0, 1, 4, 2, 777, 128)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    a = ssa.prefill(qd, kd, vd, -0.5, 128, 64, True, stats=True)
+    b = ssa.prefill(qd, kd, vd, -0.5, 128, 64, True, stats=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a["out"], b["out"]) and torch.equal(a["tile_state"], b["tile_state"])
