@@ -127,3 +127,87 @@ def prefill_parity(q_bits, k_bits, v_bits, lam, Br, Bc, causal, block_idx=None, 
     n_skip = int((state[sel] == SKIPPED).sum())
     return {"max_err_out": mo[0], "rel_l2_out": mo[1], "max_err_lse": ml[0], "exempt": n_exempt,
             "visited": n_vis, "skipped": n_skip, "gpu": g, "ref": ref}
+
+
+def decode_parity(y, lam, T, units=None, Bc=64):
+    """HIP split-K decode on the whole batch vs the oracle on (b, kvh) units."""
+    import sparse_attention_long_skip_amd as ssa
+    q, kc, vc = dev_bf16(y["q"]), dev_bf16(y["k_cache"]), dev_bf16(y["v_cache"])
+    seq = torch.from_numpy(np.asarray(y["seqlens"], np.int32)).cuda()
+    g = ssa.decode(q, kc, vc, seq, lam, split_tiles=T, Bc=Bc, stats=True, margins=True)
+    torch.cuda.synchronize()
+    ref = oracle.decode(y["q"], y["k_cache"], y["v_cache"], y["seqlens"], lam, Bc, T,
+                        units=units, bits=True)
+    B, Hq, d = y["q"].shape
+    Hkv = y["k_cache"].shape[1]
+    G = Hq // Hkv
+    if units is None:
+        units = [(b, h) for b in range(B) for h in range(Hkv)]
+    sel = tuple(np.array(units).T)
+    state = to_np(g["tile_state"])
+    n_exempt, diff = compare_decisions(state[sel], ref["decision"][sel], ref["margin"][sel], lam)
+    sc = to_np(g["skip_counts"])
+    if n_exempt == 0:
+        assert np.array_equal(sc[sel], ref["skip_counts"][sel])
+    gm = to_np(g["tile_margin"])[sel]
+    rm = ref["margin"][sel]
+    vis = ref["decision"][sel] != NOT_VISITED
+    fin = vis & np.isfinite(rm)
+    assert np.array_equal(np.isposinf(gm[vis]), np.isposinf(rm[vis]))
+    if fin.any():
+        assert np.max(np.abs(gm[fin] - rm[fin])) < 1e-3
+    replay = [u for u, dd in zip(units, diff.any(axis=-1)) if dd]
+    rep = None
+    if replay:
+        rep = oracle.decode(y["q"], y["k_cache"], y["v_cache"], y["seqlens"], lam, Bc, T,
+                            units=replay, forced=state.astype(np.int8), bits=True)
+    rs = set(replay)
+    out_g, lse_g = to_np(g["out"]), to_np(g["lse"])
+    go, ro, gl, rl = [], [], [], []
+    for (b, kvh) in units:
+        src = rep if (b, kvh) in rs else ref
+        hs = slice(kvh * G, (kvh + 1) * G)
+        go.append(out_g[b, hs]); ro.append(src["out"][b, hs])
+        gl.append(lse_g[b, hs]); rl.append(src["lse"][b, hs])
+    mo = assert_close("out", np.concatenate(go), np.concatenate(ro))
+    assert_close("lse", np.concatenate(gl), np.concatenate(rl), rtol_l2=1.0)
+    return {"max_err_out": mo[0], "rel_l2_out": mo[1], "exempt": n_exempt,
+            "visited": int(vis.sum()), "skipped": int((state[sel] == SKIPPED).sum()),
+            "gpu": g, "ref": ref}
+
+
+def mask_parity(q_bits, k_bits, pool, topk, sink, window, heads=None, band=BAND):
+    """HIP block mask vs the oracle on the listed (b, h) heads. Kept sets must
+    match except candidates whose oracle score lies within ``band`` of the
+    topk-th score of that row (near-ties)."""
+    import sparse_attention_long_skip_amd as ssa
+    q, k = dev_bf16(q_bits), dev_bf16(k_bits)
+    g = ssa.block_mask(q, k, pool, topk, sink, window, scores=True)
+    torch.cuda.synchronize()
+    B, H, L, d = q_bits.shape
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    gi, gc = to_np(g["block_idx"]), to_np(g["block_cnt"])
+    gs = to_np(g["scores"])
+    n_ties = 0
+    refs = {}
+    for (b, h) in heads:
+        r = oracle.block_mask(q_bits[b:b + 1, h:h + 1], k_bits[b:b + 1, h:h + 1], pool, topk, sink,
+                              window, bits=True)
+        refs[(b, h)] = r
+        nB = r["block_cnt"].shape[-1]
+        assert gi.shape[-1] == r["max_blocks"]
+        sc = r["scores"][0, 0]
+        fin = np.isfinite(sc)
+        assert np.array_equal(np.isfinite(gs[b, h]), fin)
+        assert np.max(np.abs(gs[b, h][fin] - sc[fin])) < 1e-4
+        for qb in range(nB):
+            got = gi[b, h, qb, :gc[b, h, qb]].tolist()
+            assert all(x == -1 for x in gi[b, h, qb, gc[b, h, qb]:])
+            assert got == sorted(set(got))
+            want = r["block_idx"][0, 0, qb, :r["block_cnt"][0, 0, qb]].tolist()
+            if got != want:
+                for c in set(got) ^ set(want):
+                    assert abs(sc[qb, c] - r["kth"][0, 0, qb]) < band, (b, h, qb, c)
+                    n_ties += 1
+    return {"ties": n_ties, "gpu": g, "refs": refs}

@@ -1,0 +1,60 @@
+"""GPU parity: split-K Skip-Softmax decode (HIP, through the C ABI) against the oracle."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import decode_parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("T", [1, 3, 100])
+def test_dense_and_calibrated_small(d, T):
+    y = synth.decode_inputs(300, d + T, 4, 8, 2, 1000, d, 1, 1000, seqlens=[1, 63, 650, 1000])
+    r = decode_parity(y, -math.inf, T)
+    assert r["skipped"] == 0
+    m = oracle.decode(y["q"], y["k_cache"], y["v_cache"], y["seqlens"], -math.inf, 64, T,
+                      bits=True)["margin"]
+    lam = oracle.lambda_for_ratio(m, 0.5)
+    r = decode_parity(y, lam, T)
+    print(f"d={d} T={T} lam={lam:.3f} skipped {r['skipped']}/{r['visited']} exempt {r['exempt']}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+def test_group_sizes(G):
+    Hkv = 2
+    y = synth.decode_inputs(301, G, 2, G * Hkv, Hkv, 2048, 128, 1500, 2048)
+    for lam in (-math.inf, -0.5):
+        decode_parity(y, lam, 8)
+
+
+def test_empty_sequence_and_nan_tail():
+    # length 0 -> out 0, lse -inf; the NaN-filled tail must never be read
+    y = synth.decode_inputs(302, 0, 3, 4, 1, 512, 128, 0, 512, seqlens=[0, 5, 512])
+    r = decode_parity(y, -1.0, 2)
+    out = r["gpu"]["out"].float().cpu().numpy()
+    assert np.all(out[0] == 0) and np.all(np.isneginf(r["gpu"]["lse"].cpu().numpy()[0]))
+    assert np.all(np.isfinite(out))
+
+
+def test_workspace_reuse_second_call_smaller():
+    import torch
+    import sparse_attention_long_skip_amd as ssa
+    from parity import dev_bf16
+    y = synth.decode_inputs(303, 0, 2, 8, 2, 4096, 128, 3000, 4096)
+    ws = torch.empty(ssa.decode_workspace_size(2, 8, 4096, 128, 64, 4), dtype=torch.uint8,
+                     device="cuda")
+    seq = torch.tensor(y["seqlens"], dtype=torch.int32, device="cuda")
+    a = ssa.decode(dev_bf16(y["q"]), dev_bf16(y["k_cache"]), dev_bf16(y["v_cache"]), seq, -1.0,
+                   split_tiles=4, workspace=ws)
+    seq2 = torch.tensor([100, 2000], dtype=torch.int32, device="cuda")
+    b = ssa.decode(dev_bf16(y["q"]), dev_bf16(y["k_cache"]), dev_bf16(y["v_cache"]), seq2, -1.0,
+                   split_tiles=4, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.decode(y["q"], y["k_cache"], y["v_cache"], [100, 2000], -1.0, 64, 4, bits=True)
+    assert np.abs(b["out"].float().cpu().numpy() - ref["out"]).max() < 2e-2
