@@ -253,6 +253,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only-main", action="store_true", help="skip extra and cpu baseline (profiling)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the main leg, copy a 1 GiB buffer 5 times (HBM counter scale)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the kernels shard by "
@@ -306,6 +308,14 @@ def main():
     }
     del p
     torch.cuda.empty_cache()
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        ms_c, ev_c = time_launches(lambda: dst.copy_(src), 5, 1, torch)
+        log(f"copy probe: 1 GiB copy {ev_c:.3f} ms ({2 * (1 << 30) / (ev_c * 1e-3) / 1e9:.1f} GB/s)")
+        result["copy_probe"] = {"bytes_read": 1 << 30, "bytes_written": 1 << 30, "ms": round(ev_c, 4)}
+        del src, dst
     extra = {}
     if not (args.no_extra or args.only_main):
         for name, fn in (("prefill_128k", extra_128k), ("decode", extra_decode), ("block_sparse_32k", extra_sparse)):

@@ -56,6 +56,24 @@ __device__ __forceinline__ float wave_sum(float x) {
 // Value held by lane (l ^ 32).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, kWave); }
 
+// max(x[l], x[l ^ 32]) for every lane, through the half-wave swap
+// (v_permlane32_swap): after swapping, one result holds the lane's own value
+// and the other the opposite half's, in either order.
+__device__ __forceinline__ float max_halves(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Number of XCDs; workgroups are dealt to them round-robin by id.
+constexpr int kNumXcd = 8;
+
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 

@@ -7,21 +7,29 @@
 //
 // Design:
 //  * One workgroup per (batch, query head, query tile of BR rows); BR/32
-//    waves, each owning 32 query rows. Heavy (late, causal) tiles launch
-//    first.
+//    waves, each owning 32 query rows; two workgroups per CU so that one
+//    workgroup's exponentials overlap the other's matrix work.
 //  * Scores are computed transposed, S^T = K Q^T, with 32x32x16 bf16 MFMA:
 //    K rows come from LDS (A operand), Q stays in registers (B operand). The
 //    accumulator then gives every lane ONE query row (lane % 32) and 16 keys
 //    per 32-key block, so row max / row sum / rescale are lane-local plus one
-//    exchange between the two half-waves.
+//    half-wave swap.
 //  * The output is accumulated transposed as well, O^T = V^T P^T: the P
 //    registers are already the B operand (same lane = query), and V is
 //    written to LDS transposed (d-major) so the A operand is two 8-byte LDS
 //    reads per lane.
-//  * K tiles are double-buffered in LDS and prefetched one tile ahead into
-//    registers. The vote: each wave reduces its rows' gaps to a max; the
-//    workgroup max decides, uniformly, whether the tile is skipped. Only then
-//    are the V loads issued, and the exp / rescale work overlaps them.
+//  * Software pipeline, one iteration per key tile t:
+//      store K(t) [and V(t-1) if kept] to LDS; barrier;
+//      prefetch K(t+1) into registers;
+//      P.V of tile t-1 (MFMA), then S(t) (MFMA);
+//      row max, gap, ballot; per-wave flag to LDS; barrier; workgroup vote;
+//      if kept: issue the V(t) loads, then exp -> P(t) (bf16, kept in
+//      registers for the next iteration), rescale O only if a row max grew.
+//    So V is fetched only for kept tiles, and its load latency is covered by
+//    the exponentials of its own tile and the matrix work of the next one.
+//  * Workgroups are mapped so that every XCD (own L2) works through whole KV
+//    heads, heaviest causal query tiles first, the G query heads of one KV
+//    head on consecutive slots: the K/V tiles they stream stay L2-resident.
 #include "common.h"
 #include "launch.h"
 
@@ -41,8 +49,9 @@ struct PrefillArgs {
   uint8_t* tile_state;
   float* tile_margin;
   int B, Hq, Hkv, L, nQ, nK, G;
-  float lam_raw;     // lambda * sqrt(d): threshold on raw q.k differences
-  float c_log2;      // log2(e) / sqrt(d)
+  int tasks, per_xcd;  // B*Hq*nQ work items; items per XCD
+  float lam_raw;       // lambda * sqrt(d): threshold on raw q.k differences
+  float c_log2;        // log2(e) / sqrt(d)
   float inv_sqrt_d;
   int causal;
   const int32_t* block_idx;
@@ -50,21 +59,24 @@ struct PrefillArgs {
   int max_blocks;
 };
 
-template <int D, int BR>
-__global__ __launch_bounds__(BR * 2) void prefill_kernel(PrefillArgs a) {
+// STATS: write per-tile decisions / margins (a separate instance, so the hot
+// instance carries none of that code).
+template <int D, int BR, bool STATS>
+__global__ __launch_bounds__(BR * 2) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_kernel(PrefillArgs a) {
   constexpr int NW = BR / 32;
   constexpr int NT = NW * kWave;
   constexpr int KP = D + 8;   // K tile row pitch in LDS (bf16 elements)
   constexpr int VP = BC + 4;  // transposed V row pitch in LDS (bf16 elements)
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int KCH = BC * D / 8 / NT;         // 16-byte K chunks per thread
-  constexpr int NVG = 16 * (D / 8);            // (4 keys x 8 d) V groups per tile
+  constexpr int KCH = BC * D / 8 / NT;  // 16-byte K chunks per thread
+  constexpr int NVG = 16 * (D / 8);     // (4 keys x 8 d) V groups per tile
   constexpr int VCH = (NVG + NT - 1) / NT;
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BC * KP];
   __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VP];
-  __shared__ float gap_lds[2][NW];
+  __shared__ float flag_lds[2][NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -72,11 +84,17 @@ __global__ __launch_bounds__(BR * 2) void prefill_kernel(PrefillArgs a) {
   const int h = lane >> 5;
   const int r32 = lane & 31;
 
-  int bid = blockIdx.x;
-  const int hq = bid % a.Hq;
-  bid /= a.Hq;
-  const int i = a.nQ - 1 - (bid % a.nQ);
-  const int b = bid / a.nQ;
+  // XCD-aware work mapping: XCD x takes items [x*per_xcd, (x+1)*per_xcd).
+  const int xcd = blockIdx.x % kNumXcd;
+  const int slot = blockIdx.x / kNumXcd;
+  const int task = xcd * a.per_xcd + slot;
+  if (slot >= a.per_xcd || task >= a.tasks) return;
+  const int per_bkv = a.G * a.nQ;
+  const int bkv = task / per_bkv;
+  const int rem = task - bkv * per_bkv;
+  const int i = a.nQ - 1 - rem / a.G;  // heaviest query tiles first
+  const int hq = (bkv % a.Hkv) * a.G + rem % a.G;
+  const int b = bkv / a.Hkv;
   const int kvh = hq / a.G;
   const int L = a.L;
   const int q0 = i * BR;
@@ -129,21 +147,72 @@ __global__ __launch_bounds__(BR * 2) void prefill_kernel(PrefillArgs a) {
       kreg[r] = x;
     }
   };
-  auto store_k = [&](uint16_t* dst) {
+  u32x4 vreg[VCH][4];
+  auto load_v = [&](int j) {
 #pragma unroll
-    for (int r = 0; r < KCH; ++r) {
+    for (int r = 0; r < VCH; ++r) {
       const int id = tid + NT * r;
-      store16(dst + (id / (D / 8)) * KP + (id % (D / 8)) * 8, kreg[r]);
+      const int g4 = id & 15;
+      const int c = id >> 4;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int key = j * BC + 4 * g4 + rr;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if ((NVG % NT == 0 || id < NVG) && key < L) x = load16(vp + (size_t)key * D + c * 8);
+        vreg[r][rr] = x;
+      }
+    }
+  };
+  // V tile -> LDS, transposed to [d][key]: 4 keys x 8 d per thread group.
+  auto store_vt = [&]() {
+#pragma unroll
+    for (int r = 0; r < VCH; ++r) {
+      const int id = tid + NT * r;
+      if (NVG % NT == 0 || id < NVG) {
+        const int g4 = id & 15;
+        const int c = id >> 4;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t a0 = vreg[r][0][m], a1 = vreg[r][1][m], a2 = vreg[r][2][m], a3 = vreg[r][3][m];
+          u32x2 lo, hi;
+          lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+          lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+          hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+          hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
+          *reinterpret_cast<u32x2*>(vt_lds + (c * 8 + 2 * m) * VP + 4 * g4) = lo;
+          *reinterpret_cast<u32x2*>(vt_lds + (c * 8 + 2 * m + 1) * VP + 4 * g4) = hi;
+        }
+      }
     }
   };
 
-  float m_prev = -INFINITY;  // running max of raw q.k for this lane's row
-  float l_acc = 0.f;         // partial row sum over this lane's keys
+  float m_run = -INFINITY;  // running max of raw q.k for this lane's row
+  float l_acc = 0.f;        // partial row sum over this lane's keys
   f32x16 o[NDB];
 #pragma unroll
   for (int nb = 0; nb < NDB; ++nb)
+#pragma unroll
     for (int e = 0; e < 16; ++e) o[nb][e] = 0.f;
+  bf16x8 p[4];  // P of the pending (kept, not yet multiplied) tile
+  bool pending = false;
   int skipped = 0;
+
+  auto pv = [&]() {
+#pragma unroll
+    for (int nb = 0; nb < NDB; ++nb) {
+      const uint16_t* vrow = vt_lds + (nb * 32 + r32) * VP + h * 4;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          const int kc = kb * 32 + gp * 16;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kc);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + kc + 8);
+          u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+          o[nb] = mfma32(as_bf16x8(va), p[kb * 2 + gp], o[nb]);
+        }
+    }
+  };
 
   int t = next_valid(0);
   if (t < n_list) load_k(tile_of(t));
@@ -153,14 +222,21 @@ __global__ __launch_bounds__(BR * 2) void prefill_kernel(PrefillArgs a) {
     const int tn = next_valid(t + 1);
     const int buf = it & 1;
     uint16_t* kl = k_lds[buf];
-    store_k(kl);
+#pragma unroll
+    for (int r = 0; r < KCH; ++r) {
+      const int id = tid + NT * r;
+      store16(kl + (id / (D / 8)) * KP + (id % (D / 8)) * 8, kreg[r]);
+    }
+    if (pending) store_vt();
     __syncthreads();
     if (tn < n_list) load_k(tile_of(tn));
+    if (pending) pv();
 
     // S^T = K Q^T for this wave's 32 rows and the tile's 64 keys.
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
       for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
@@ -184,46 +260,43 @@ __global__ __launch_bounds__(BR * 2) void prefill_kernel(PrefillArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, s[kb][e]);
-    mloc = fmaxf(mloc, swap_halves(mloc));
+    mloc = max_halves(mloc);
     float gap;
     if (!row_ok || mloc == -INFINITY) gap = -INFINITY;
-    else if (m_prev == -INFINITY) gap = INFINITY;
-    else gap = mloc - m_prev;
-    gap = wave_max(gap);
-    if (lane == 0) gap_lds[buf][w] = gap;
+    else if (m_run == -INFINITY) gap = INFINITY;
+    else gap = mloc - m_run;
+    if (STATS) {
+      const float gw = wave_max(gap);
+      if (lane == 0) flag_lds[buf][w] = gw;
+    } else {
+      const bool wk = __ballot(gap >= a.lam_raw) != 0ull;
+      if (lane == 0) flag_lds[buf][w] = wk ? 1.f : 0.f;
+    }
     __syncthreads();
-    float g = gap_lds[buf][0];
+    bool keep;
+    if (STATS) {
+      float g = flag_lds[buf][0];
 #pragma unroll
-    for (int ww = 1; ww < NW; ++ww) g = fmaxf(g, gap_lds[buf][ww]);
-    const bool skip = g < a.lam_raw;
-    if (tid == 0) {
-      const size_t ti = unit * a.nK + j;
-      if (a.tile_state) a.tile_state[ti] = skip ? 2 : 1;
-      if (a.tile_margin) a.tile_margin[ti] = g * a.inv_sqrt_d;
+      for (int ww = 1; ww < NW; ++ww) g = fmaxf(g, flag_lds[buf][ww]);
+      keep = !(g < a.lam_raw);
+      if (tid == 0) {
+        const size_t ti = unit * a.nK + j;
+        if (a.tile_state) a.tile_state[ti] = keep ? 1 : 2;
+        if (a.tile_margin) a.tile_margin[ti] = g * a.inv_sqrt_d;
+      }
+    } else {
+      float f = flag_lds[buf][0];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) f += flag_lds[buf][ww];
+      keep = f > 0.f;
     }
 
-    if (!skip) {
-      // V loads for this tile: 4 consecutive keys x 8 d per group.
-      u32x4 vreg[VCH][4];
-#pragma unroll
-      for (int r = 0; r < VCH; ++r) {
-        const int id = tid + NT * r;
-        const int g4 = id & 15;
-        const int c = id >> 4;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int key = kbase + 4 * g4 + rr;
-          u32x4 x = {0u, 0u, 0u, 0u};
-          if ((NVG % NT == 0 || id < NVG) && key < L) x = load16(vp + (size_t)key * D + c * 8);
-          vreg[r][rr] = x;
-        }
-      }
-      // Online softmax update (exp2 with the 1/sqrt(d) and log2(e) folded in).
-      const float m_new = fmaxf(m_prev, mloc);
+    const float m_new = fmaxf(m_run, mloc);
+    if (keep) {
+      load_v(j);
+      // Online softmax update, exp2 with 1/sqrt(d) and log2(e) folded in.
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2((m_prev - m_use) * a.c_log2);
       const float mc = m_use * a.c_log2;
-      bf16x8 p[4];
       float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -239,59 +312,33 @@ __global__ __launch_bounds__(BR * 2) void prefill_kernel(PrefillArgs a) {
           }
           p[kb * 2 + gp] = as_bf16x8(pk);
         }
-      l_acc = l_acc * alpha + psum;
+      if (__ballot(m_new != m_run) != 0ull) {
+        const float alpha = fast_exp2((m_run - m_use) * a.c_log2);
+        l_acc *= alpha;
 #pragma unroll
-      for (int nb = 0; nb < NDB; ++nb)
+        for (int nb = 0; nb < NDB; ++nb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[nb][e] *= alpha;
-      m_prev = m_new;
-
-      // V tile -> LDS, transposed to [d][key].
-#pragma unroll
-      for (int r = 0; r < VCH; ++r) {
-        const int id = tid + NT * r;
-        if (NVG % NT == 0 || id < NVG) {
-          const int g4 = id & 15;
-          const int c = id >> 4;
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const uint32_t a0 = vreg[r][0][m], a1 = vreg[r][1][m], a2 = vreg[r][2][m], a3 = vreg[r][3][m];
-            u32x2 lo, hi;
-            lo[0] = (a0 & 0xffffu) | (a1 << 16);
-            lo[1] = (a2 & 0xffffu) | (a3 << 16);
-            hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-            hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-            *reinterpret_cast<u32x2*>(vt_lds + (c * 8 + 2 * m) * VP + 4 * g4) = lo;
-            *reinterpret_cast<u32x2*>(vt_lds + (c * 8 + 2 * m + 1) * VP + 4 * g4) = hi;
-          }
-        }
+          for (int e = 0; e < 16; ++e) o[nb][e] *= alpha;
       }
-      __syncthreads();
-      // O^T += V^T P^T
-#pragma unroll
-      for (int nb = 0; nb < NDB; ++nb) {
-        const uint16_t* vrow = vt_lds + (nb * 32 + r32) * VP + h * 4;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int gp = 0; gp < 2; ++gp) {
-            const int kc = kb * 32 + gp * 16;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kc);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + kc + 8);
-            u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-            o[nb] = mfma32(as_bf16x8(va), p[kb * 2 + gp], o[nb]);
-          }
-      }
+      l_acc += psum;
+      pending = true;
     } else {
       ++skipped;
-      m_prev = fmaxf(m_prev, mloc);
+      pending = false;
     }
+    m_run = m_new;
     t = tn;
     ++it;
   }
+  if (pending) {
+    __syncthreads();  // every wave is past its last read of vt_lds
+    store_vt();
+    __syncthreads();
+    pv();
+  }
 
   // Epilogue: normalise, write out (bf16) and lse.
-  const float l_tot = l_acc + swap_halves(l_acc);
+  const float l_tot = sum_halves(l_acc);
   if (row_ok) {
     const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* op = a.out + ((size_t)(b * a.Hq + hq) * L + row) * D;
@@ -306,16 +353,19 @@ __global__ __launch_bounds__(BR * 2) void prefill_kernel(PrefillArgs a) {
       }
     if (a.lse && h == 0)
       a.lse[(size_t)(b * a.Hq + hq) * L + row] =
-          l_tot > 0.f ? m_prev * a.inv_sqrt_d + __logf(l_tot) : -INFINITY;
+          l_tot > 0.f ? m_run * a.inv_sqrt_d + __logf(l_tot) : -INFINITY;
   }
   if (a.skip_counts && tid == 0) a.skip_counts[unit] = skipped;
 }
 
 template <int D, int BR>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
-  dim3 grid((unsigned)((size_t)a.B * a.Hq * a.nQ));
+  dim3 grid((unsigned)(a.per_xcd * kNumXcd));
   dim3 block(BR * 2);
-  hipLaunchKernelGGL((prefill_kernel<D, BR>), grid, block, 0, stream, a);
+  if (a.tile_state || a.tile_margin)
+    hipLaunchKernelGGL((prefill_kernel<D, BR, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, BR, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -338,6 +388,8 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   a.nQ = (p.L + p.Br - 1) / p.Br;
   a.nK = (p.L + p.Bc - 1) / p.Bc;
   a.G = p.Hq / p.Hkv;
+  a.tasks = p.B * p.Hq * a.nQ;
+  a.per_xcd = (a.tasks + kNumXcd - 1) / kNumXcd;
   const float sd = sqrtf((float)p.d);
   a.lam_raw = p.lambda * sd;
   a.c_log2 = kLog2e / sd;
