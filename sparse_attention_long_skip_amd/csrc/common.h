@@ -74,6 +74,35 @@ __device__ __forceinline__ float sum_halves(float x) {
 // Number of XCDs; workgroups are dealt to them round-robin by id.
 constexpr int kNumXcd = 8;
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Two fp32 -> one packed bf16 pair with a single conversion (RNE).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Asynchronous 16-byte global -> LDS copy: lane i's chunk lands at
+// lds_base + 16 * i (lds_base must be wave-uniform).
+__device__ __forceinline__ void load_lds16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)gsrc,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// Wait until every global load of this wave (including LDS-direct ones) is done.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane li receives element (li % 4) of the 8-byte chunks addressed by lanes
+// 4e + li / 4, for e = 0..3.
+__device__ __forceinline__ uint64_t lds_read_tr16(const void* lds_addr) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(lds_addr));
+  return __builtin_bit_cast(uint64_t, v);
+}
+
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 

@@ -15,18 +15,21 @@
 //    per 32-key block, so row max / row sum / rescale are lane-local plus one
 //    half-wave swap.
 //  * The output is accumulated transposed as well, O^T = V^T P^T: the P
-//    registers are already the B operand (same lane = query), and V is
-//    written to LDS transposed (d-major) so the A operand is two 8-byte LDS
-//    reads per lane.
+//    registers are already the B operand (same lane = query), and the V^T
+//    A operand comes straight from the row-major V tile in LDS through the
+//    transposing LDS read (ds_read_b64_tr_b16).
+//  * K and V tiles go from HBM to LDS with LDS-direct 16-byte loads (no
+//    staging registers), into XOR-swizzled rows so that both the K row reads
+//    and the transposing V reads are free of bank conflicts. K and V are
+//    double-buffered.
 //  * Software pipeline, one iteration per key tile t:
-//      store K(t) [and V(t-1) if kept] to LDS; barrier;
-//      prefetch K(t+1) into registers;
-//      P.V of tile t-1 (MFMA), then S(t) (MFMA);
-//      row max, gap, ballot; per-wave flag to LDS; barrier; workgroup vote;
-//      if kept: issue the V(t) loads, then exp -> P(t) (bf16, kept in
-//      registers for the next iteration), rescale O only if a row max grew.
-//    So V is fetched only for kept tiles, and its load latency is covered by
-//    the exponentials of its own tile and the matrix work of the next one.
+//      wait for this wave's loads; barrier (K(t), V(t-1) visible);
+//      issue K(t+1) loads; S(t) (MFMA); row max, gap, ballot; barrier;
+//      workgroup vote; if kept: issue V(t) loads;
+//      P.V of tile t-1 (MFMA); if kept: exp -> P(t) (bf16 registers),
+//      rescale O only if a row max grew.
+//    So V is fetched only for kept tiles, and its latency is covered by the
+//    previous tile's P.V and this tile's exponentials.
 //  * Workgroups are mapped so that every XCD (own L2) works through whole KV
 //    heads, heaviest causal query tiles first, the G query heads of one KV
 //    head on consecutive slots: the K/V tiles they stream stay L2-resident.
@@ -59,6 +62,13 @@ struct PrefillArgs {
   int max_blocks;
 };
 
+// 16-byte chunk swizzles of a tile row (physical chunk = logical ^ swz(row)).
+// K rows are read 16 rows x one chunk at a time; V rows 4 rows x 4 chunks.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
 // STATS: write per-tile decisions / margins (a separate instance, so the hot
 // instance carries none of that code).
 template <int D, int BR, bool STATS>
@@ -66,16 +76,14 @@ __global__ __launch_bounds__(BR * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillArgs a) {
   constexpr int NW = BR / 32;
   constexpr int NT = NW * kWave;
-  constexpr int KP = D + 8;   // K tile row pitch in LDS (bf16 elements)
-  constexpr int VP = BC + 4;  // transposed V row pitch in LDS (bf16 elements)
+  constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  constexpr int TILE = BC * D;                 // bf16 elements per K or V tile
+  constexpr int LPW = TILE * 2 / 1024 / NW;    // 1 KiB LDS-direct loads per wave per tile
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int KCH = BC * D / 8 / NT;  // 16-byte K chunks per thread
-  constexpr int NVG = 16 * (D / 8);     // (4 keys x 8 d) V groups per tile
-  constexpr int VCH = (NVG + NT - 1) / NT;
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BC * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VP];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][TILE];
   __shared__ float flag_lds[2][NW];
 
   const int tid = threadIdx.x;
@@ -135,54 +143,17 @@ void prefill_kernel(PrefillArgs a) {
     return t;
   };
 
-  u32x4 kreg[KCH];
-  auto load_k = [&](int j) {
+  // LDS-direct tile load: this wave fills LPW consecutive 1 KiB blocks; LDS
+  // slot s (16 B) holds row s / CPR, logical chunk (s % CPR) ^ swz(row).
+  // Rows past L read row L-1 (finite data; the scores are masked and P = 0).
+  auto load_tile = [&](const uint16_t* src, int j, uint16_t* dst, bool is_k) {
 #pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int id = tid + NT * r;
-      const int key = j * BC + id / (D / 8);
-      const int c = id % (D / 8);
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < L) x = load16(kp + (size_t)key * D + c * 8);
-      kreg[r] = x;
-    }
-  };
-  u32x4 vreg[VCH][4];
-  auto load_v = [&](int j) {
-#pragma unroll
-    for (int r = 0; r < VCH; ++r) {
-      const int id = tid + NT * r;
-      const int g4 = id & 15;
-      const int c = id >> 4;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = j * BC + 4 * g4 + rr;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if ((NVG % NT == 0 || id < NVG) && key < L) x = load16(vp + (size_t)key * D + c * 8);
-        vreg[r][rr] = x;
-      }
-    }
-  };
-  // V tile -> LDS, transposed to [d][key]: 4 keys x 8 d per thread group.
-  auto store_vt = [&]() {
-#pragma unroll
-    for (int r = 0; r < VCH; ++r) {
-      const int id = tid + NT * r;
-      if (NVG % NT == 0 || id < NVG) {
-        const int g4 = id & 15;
-        const int c = id >> 4;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t a0 = vreg[r][0][m], a1 = vreg[r][1][m], a2 = vreg[r][2][m], a3 = vreg[r][3][m];
-          u32x2 lo, hi;
-          lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-          lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-          hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-          hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-          *reinterpret_cast<u32x2*>(vt_lds + (c * 8 + 2 * m) * VP + 4 * g4) = lo;
-          *reinterpret_cast<u32x2*>(vt_lds + (c * 8 + 2 * m + 1) * VP + 4 * g4) = hi;
-        }
-      }
+    for (int r = 0; r < LPW; ++r) {
+      const int s = (w * LPW + r) * 64 + lane;
+      const int rr = s / CPR;
+      const int c = (s % CPR) ^ (is_k ? swz_k<D>(rr) : swz_v<D>(rr));
+      const int key = min(j * BC + rr, L - 1);
+      load_lds16(src + (size_t)key * D + c * 8, dst + (w * LPW + r) * 512);
     }
   };
 
@@ -195,42 +166,44 @@ void prefill_kernel(PrefillArgs a) {
     for (int e = 0; e < 16; ++e) o[nb][e] = 0.f;
   bf16x8 p[4];  // P of the pending (kept, not yet multiplied) tile
   bool pending = false;
+  int pbuf = 0;
   int skipped = 0;
 
-  auto pv = [&]() {
+  // O^T += V^T P^T from V buffer vb. A operand for (nb, kb, gp): element e
+  // of lane (h, r32) = V[kc + 8*(e/4) + 4h + e%4][32 nb + r32].
+  auto pv = [&](int vb) {
+    const uint16_t* vt = v_lds[vb];
+    const int g16 = lane >> 4;
+    const int jj = lane & 15;
 #pragma unroll
-    for (int nb = 0; nb < NDB; ++nb) {
-      const uint16_t* vrow = vt_lds + (nb * 32 + r32) * VP + h * 4;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int gp = 0; gp < 2; ++gp) {
+        const int kc = kb * 32 + gp * 16;
 #pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-          const int kc = kb * 32 + gp * 16;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kc);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + kc + 8);
-          u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+        for (int nb = 0; nb < NDB; ++nb) {
+          const int c = nb * 4 + (g16 & 1) * 2 + ((jj & 3) >> 1);
+          const int ra = kc + 4 * h + (jj >> 2);
+          const int rb = ra + 8;
+          const uint64_t lo = lds_read_tr16(vt + ra * D + ((c ^ swz_v<D>(ra)) * 8) + (jj & 1) * 4);
+          const uint64_t hi = lds_read_tr16(vt + rb * D + ((c ^ swz_v<D>(rb)) * 8) + (jj & 1) * 4);
+          u32x4 va = {(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
           o[nb] = mfma32(as_bf16x8(va), p[kb * 2 + gp], o[nb]);
         }
-    }
+      }
   };
 
   int t = next_valid(0);
-  if (t < n_list) load_k(tile_of(t));
+  if (t < n_list) load_tile(kp, tile_of(t), k_lds[0], true);
   int it = 0;
   while (t < n_list) {
     const int j = tile_of(t);
     const int tn = next_valid(t + 1);
     const int buf = it & 1;
-    uint16_t* kl = k_lds[buf];
-#pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int id = tid + NT * r;
-      store16(kl + (id / (D / 8)) * KP + (id % (D / 8)) * 8, kreg[r]);
-    }
-    if (pending) store_vt();
+    const uint16_t* kl = k_lds[buf];
+    wait_vmem();
     __syncthreads();
-    if (tn < n_list) load_k(tile_of(tn));
-    if (pending) pv();
+    if (tn < n_list) load_tile(kp, tile_of(tn), k_lds[buf ^ 1], true);
 
     // S^T = K Q^T for this wave's 32 rows and the tile's 64 keys.
     f32x16 s[2];
@@ -238,9 +211,11 @@ void prefill_kernel(PrefillArgs a) {
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+      const int kr = kb * 32 + r32;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        bf16x8 ka = as_bf16x8(load16(kl + (kb * 32 + r32) * KP + kk * 16 + h * 8));
+        const int c = (2 * kk + h) ^ swz_k<D>(kr);
+        bf16x8 ka = as_bf16x8(load16(kl + kr * D + c * 8));
         s[kb] = mfma32(ka, qf[kk], s[kb]);
       }
     }
@@ -290,10 +265,11 @@ void prefill_kernel(PrefillArgs a) {
       for (int ww = 1; ww < NW; ++ww) f += flag_lds[buf][ww];
       keep = f > 0.f;
     }
+    if (keep) load_tile(vp, j, v_lds[buf], false);
+    if (pending) pv(pbuf);
 
     const float m_new = fmaxf(m_run, mloc);
     if (keep) {
-      load_v(j);
       // Online softmax update, exp2 with 1/sqrt(d) and log2(e) folded in.
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float mc = m_use * a.c_log2;
@@ -308,7 +284,7 @@ void prefill_kernel(PrefillArgs a) {
             const float x0 = fast_exp2(fmaf(s[kb][gp * 8 + e], a.c_log2, -mc));
             const float x1 = fast_exp2(fmaf(s[kb][gp * 8 + e + 1], a.c_log2, -mc));
             psum += x0 + x1;
-            pk[e >> 1] = pack_bf16x2(x0, x1);
+            pk[e >> 1] = cvt_pk_bf16(x0, x1);
           }
           p[kb * 2 + gp] = as_bf16x8(pk);
         }
@@ -321,20 +297,19 @@ void prefill_kernel(PrefillArgs a) {
           for (int e = 0; e < 16; ++e) o[nb][e] *= alpha;
       }
       l_acc += psum;
-      pending = true;
+      pbuf = buf;
     } else {
       ++skipped;
-      pending = false;
     }
+    pending = keep;
     m_run = m_new;
     t = tn;
     ++it;
   }
   if (pending) {
-    __syncthreads();  // every wave is past its last read of vt_lds
-    store_vt();
+    wait_vmem();
     __syncthreads();
-    pv();
+    pv(pbuf);
   }
 
   // Epilogue: normalise, write out (bf16) and lse.
@@ -347,8 +322,8 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         u32x2 st;
-        st[0] = pack_bf16x2(o[nb][g4 * 4 + 0] * inv_l, o[nb][g4 * 4 + 1] * inv_l);
-        st[1] = pack_bf16x2(o[nb][g4 * 4 + 2] * inv_l, o[nb][g4 * 4 + 3] * inv_l);
+        st[0] = cvt_pk_bf16(o[nb][g4 * 4 + 0] * inv_l, o[nb][g4 * 4 + 1] * inv_l);
+        st[1] = cvt_pk_bf16(o[nb][g4 * 4 + 2] * inv_l, o[nb][g4 * 4 + 3] * inv_l);
         *reinterpret_cast<u32x2*>(op + nb * 32 + g4 * 8 + h * 4) = st;
       }
     if (a.lse && h == 0)
