@@ -22,14 +22,18 @@
 //    staging registers), into XOR-swizzled rows so that both the K row reads
 //    and the transposing V reads are free of bank conflicts. K and V are
 //    double-buffered.
-//  * Software pipeline, one iteration per key tile t:
-//      wait for this wave's loads; barrier (K(t), V(t-1) visible);
-//      issue K(t+1) loads; S(t) (MFMA); row max, gap, ballot; barrier;
-//      workgroup vote; if kept: issue V(t) loads;
-//      P.V of tile t-1 (MFMA); if kept: exp -> P(t) (bf16 registers),
-//      rescale O only if a row max grew.
-//    So V is fetched only for kept tiles, and its latency is covered by the
-//    previous tile's P.V and this tile's exponentials.
+//  * Software pipeline over the visited tiles, ONE barrier per step t:
+//      wait for this wave's loads; barrier (K(t), V(t-2), flags(t-1) visible);
+//      workgroup vote of tile t-1 (OR of the per-wave ballots); if kept,
+//      issue the V(t-1) loads; issue the K(t+1) loads; P.V of tile t-2
+//      (MFMA); if tile t-1 is kept, exp -> P(t-1) (bf16 registers); scores of
+//      tile t (MFMA), row max, gap against the running max, wave ballot.
+//    So V is fetched only for kept tiles and has a whole step to land, and
+//    the exponentials of one tile sit between two blocks of matrix work.
+//  * The exponentials use a reference max that lags the running max: O and
+//    the row sum are rescaled only when a row max exceeds the reference by
+//    more than 2^8 in the exp2 domain (softmax is exact for any reference;
+//    P stays <= 256).
 //  * Workgroups are mapped so that every XCD (own L2) works through whole KV
 //    heads, heaviest causal query tiles first, the G query heads of one KV
 //    head on consecutive slots: the K/V tiles they stream stay L2-resident.
@@ -143,30 +147,49 @@ void prefill_kernel(PrefillArgs a) {
     return t;
   };
 
-  // LDS-direct tile load: this wave fills LPW consecutive 1 KiB blocks; LDS
+  // LDS-direct tile loads: this wave fills LPW consecutive 1 KiB blocks; LDS
   // slot s (16 B) holds row s / CPR, logical chunk (s % CPR) ^ swz(row).
-  // Rows past L read row L-1 (finite data; the scores are masked and P = 0).
-  auto load_tile = [&](const uint16_t* src, int j, uint16_t* dst, bool is_k) {
+  // Per-lane source offsets are fixed; rows past L (last tile only) read
+  // row L-1 (finite data; those scores are masked and their P is 0).
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  int koff[LPW], voff[LPW], lrow[LPW];
 #pragma unroll
-    for (int r = 0; r < LPW; ++r) {
-      const int s = (w * LPW + r) * 64 + lane;
-      const int rr = s / CPR;
-      const int c = (s % CPR) ^ (is_k ? swz_k<D>(rr) : swz_v<D>(rr));
-      const int key = min(j * BC + rr, L - 1);
-      load_lds16(src + (size_t)key * D + c * 8, dst + (w * LPW + r) * 512);
+  for (int r = 0; r < LPW; ++r) {
+    const int s = (w * LPW + r) * 64 + lane;
+    const int rr = s / CPR;
+    lrow[r] = rr;
+    koff[r] = rr * D + ((s % CPR) ^ swz_k<D>(rr)) * 8;
+    voff[r] = rr * D + ((s % CPR) ^ swz_v<D>(rr)) * 8;
+  }
+  auto load_tile = [&](const uint16_t* src, int j, uint16_t* dst, const int* off) {
+    const int kb0 = j * BC;
+    const uint16_t* base = src + (size_t)kb0 * D;
+    if (kb0 + BC <= L) {
+#pragma unroll
+      for (int r = 0; r < LPW; ++r) load_lds16(base + off[r], dst + (wu * LPW + r) * 512);
+    } else {
+#pragma unroll
+      for (int r = 0; r < LPW; ++r) {
+        const int over = max(kb0 + lrow[r] - (L - 1), 0);
+        load_lds16(base + off[r] - (size_t)over * D, dst + (wu * LPW + r) * 512);
+      }
     }
   };
 
-  float m_run = -INFINITY;  // running max of raw q.k for this lane's row
-  float l_acc = 0.f;        // partial row sum over this lane's keys
+  float m_run = -INFINITY;  // running max of raw q.k over visited tiles (the vote)
+  float m_ref = -INFINITY;  // reference max of the exponentials (lags m_run)
+  float l_acc = 0.f;        // partial row sum over this lane's keys, relative to m_ref
+  // Rescale O only when a row max exceeds the reference by more than 2^8 in
+  // the exp2 domain; P <= 256 otherwise. Softmax is exact for any reference.
+  const float tau_raw = 8.f / a.c_log2;
   f32x16 o[NDB];
 #pragma unroll
   for (int nb = 0; nb < NDB; ++nb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[nb][e] = 0.f;
-  bf16x8 p[4];  // P of the pending (kept, not yet multiplied) tile
-  bool pending = false;
-  int pbuf = 0;
+  f32x16 s[2];  // scores of the latest tile
+  bf16x8 p[4];  // P of the kept tile awaiting its P.V
+  bool keep2 = false;
   int skipped = 0;
 
   // O^T += V^T P^T from V buffer vb. A operand for (nb, kb, gp): element e
@@ -193,86 +216,58 @@ void prefill_kernel(PrefillArgs a) {
       }
   };
 
-  int t = next_valid(0);
-  if (t < n_list) load_tile(kp, tile_of(t), k_lds[0], true);
+  // Pipeline over list positions t = 0 .. n+1, one barrier each:
+  //   vote of tile t-1 -> issue V(t-1); issue K(t+1); P.V of tile t-2;
+  //   exp of tile t-1; scores, row max and wave flag of tile t.
+  int tcur = next_valid(0);
+  if (tcur < n_list) load_tile(kp, tile_of(tcur), k_lds[0], koff);
+  int tnext = tcur < n_list ? next_valid(tcur + 1) : n_list;
+  int jprev = -1;  // tile of the previous position
   int it = 0;
-  while (t < n_list) {
-    const int j = tile_of(t);
-    const int tn = next_valid(t + 1);
+  for (;; ++it) {
+    const bool have_cur = tcur < n_list;
+    const bool have_prev = jprev >= 0;
+    if (!have_cur && !have_prev && !keep2) break;
     const int buf = it & 1;
-    const uint16_t* kl = k_lds[buf];
     wait_vmem();
     __syncthreads();
-    if (tn < n_list) load_tile(kp, tile_of(tn), k_lds[buf ^ 1], true);
-
-    // S^T = K Q^T for this wave's 32 rows and the tile's 64 keys.
-    f32x16 s[2];
+    bool keep1 = false;
+    if (have_prev) {
+      if (STATS) {
+        float g = flag_lds[buf ^ 1][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-      const int kr = kb * 32 + r32;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const int c = (2 * kk + h) ^ swz_k<D>(kr);
-        bf16x8 ka = as_bf16x8(load16(kl + kr * D + c * 8));
-        s[kb] = mfma32(ka, qf[kk], s[kb]);
-      }
-    }
-    const int kbase = j * BC;
-    const bool need_mask = (kbase + BC > L) || (a.causal && kbase + BC - 1 > q0 + w * 32);
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kbase + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
-          if (key >= L || (a.causal && key > row)) s[kb][e] = -INFINITY;
+        for (int ww = 1; ww < NW; ++ww) g = fmaxf(g, flag_lds[buf ^ 1][ww]);
+        keep1 = !(g < a.lam_raw);
+        if (tid == 0) {
+          const size_t ti = unit * a.nK + jprev;
+          if (a.tile_state) a.tile_state[ti] = keep1 ? 1 : 2;
+          if (a.tile_margin) a.tile_margin[ti] = g * a.inv_sqrt_d;
         }
-    }
-    float mloc = -INFINITY;
+      } else {
+        float f = flag_lds[buf ^ 1][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, s[kb][e]);
-    mloc = max_halves(mloc);
-    float gap;
-    if (!row_ok || mloc == -INFINITY) gap = -INFINITY;
-    else if (m_run == -INFINITY) gap = INFINITY;
-    else gap = mloc - m_run;
-    if (STATS) {
-      const float gw = wave_max(gap);
-      if (lane == 0) flag_lds[buf][w] = gw;
-    } else {
-      const bool wk = __ballot(gap >= a.lam_raw) != 0ull;
-      if (lane == 0) flag_lds[buf][w] = wk ? 1.f : 0.f;
-    }
-    __syncthreads();
-    bool keep;
-    if (STATS) {
-      float g = flag_lds[buf][0];
-#pragma unroll
-      for (int ww = 1; ww < NW; ++ww) g = fmaxf(g, flag_lds[buf][ww]);
-      keep = !(g < a.lam_raw);
-      if (tid == 0) {
-        const size_t ti = unit * a.nK + j;
-        if (a.tile_state) a.tile_state[ti] = keep ? 1 : 2;
-        if (a.tile_margin) a.tile_margin[ti] = g * a.inv_sqrt_d;
+        for (int ww = 1; ww < NW; ++ww) f += flag_lds[buf ^ 1][ww];
+        keep1 = f > 0.f;
       }
-    } else {
-      float f = flag_lds[buf][0];
-#pragma unroll
-      for (int ww = 1; ww < NW; ++ww) f += flag_lds[buf][ww];
-      keep = f > 0.f;
+      if (keep1) load_tile(vp, jprev, v_lds[buf ^ 1], voff);
+      else ++skipped;
     }
-    if (keep) load_tile(vp, j, v_lds[buf], false);
-    if (pending) pv(pbuf);
-
-    const float m_new = fmaxf(m_run, mloc);
-    if (keep) {
-      // Online softmax update, exp2 with 1/sqrt(d) and log2(e) folded in.
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float mc = m_use * a.c_log2;
+    if (tnext < n_list) load_tile(kp, tile_of(tnext), k_lds[buf ^ 1], koff);
+    if (keep2) pv(buf);
+    if (keep1) {
+      // exp2 with 1/sqrt(d) and log2(e) folded in, against the reference max.
+      const bool grow = (m_run > m_ref + tau_raw) || (m_ref == -INFINITY && m_run != -INFINITY);
+      if (__ballot(grow) != 0ull) {
+        const float m_tgt = grow ? m_run : m_ref;
+        const float alpha = (m_ref == -INFINITY) ? 0.f : fast_exp2((m_ref - m_tgt) * a.c_log2);
+        l_acc *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NDB; ++nb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[nb][e] *= alpha;
+        m_ref = m_tgt;
+      }
+      const float mc = (m_ref == -INFINITY ? 0.f : m_ref) * a.c_log2;
       float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -288,28 +283,59 @@ void prefill_kernel(PrefillArgs a) {
           }
           p[kb * 2 + gp] = as_bf16x8(pk);
         }
-      if (__ballot(m_new != m_run) != 0ull) {
-        const float alpha = fast_exp2((m_run - m_use) * a.c_log2);
-        l_acc *= alpha;
-#pragma unroll
-        for (int nb = 0; nb < NDB; ++nb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[nb][e] *= alpha;
-      }
       l_acc += psum;
-      pbuf = buf;
-    } else {
-      ++skipped;
     }
-    pending = keep;
-    m_run = m_new;
-    t = tn;
-    ++it;
-  }
-  if (pending) {
-    wait_vmem();
-    __syncthreads();
-    pv(pbuf);
+    keep2 = keep1;
+    jprev = -1;
+    if (have_cur) {
+      const int j = tile_of(tcur);
+      const uint16_t* kl = k_lds[buf];
+      // S^T = K Q^T for this wave's 32 rows and the tile's 64 keys.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+        const int kr = kb * 32 + r32;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const int c = (2 * kk + h) ^ swz_k<D>(kr);
+          bf16x8 ka = as_bf16x8(load16(kl + kr * D + c * 8));
+          s[kb] = mfma32(ka, qf[kk], s[kb]);
+        }
+      }
+      const int kbase = j * BC;
+      const bool need_mask = (kbase + BC > L) || (a.causal && kbase + BC - 1 > q0 + w * 32);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kbase + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
+            if (key >= L || (a.causal && key > row)) s[kb][e] = -INFINITY;
+          }
+      }
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, s[kb][e]);
+      mloc = max_halves(mloc);
+      float gap;
+      if (!row_ok || mloc == -INFINITY) gap = -INFINITY;
+      else if (m_run == -INFINITY) gap = INFINITY;
+      else gap = mloc - m_run;
+      if (STATS) {
+        const float gw = wave_max(gap);
+        if (lane == 0) flag_lds[buf][w] = gw;
+      } else {
+        const bool wk = __ballot(gap >= a.lam_raw) != 0ull;
+        if (lane == 0) flag_lds[buf][w] = wk ? 1.f : 0.f;
+      }
+      m_run = fmaxf(m_run, mloc);
+      jprev = j;
+      tcur = tnext;
+      tnext = tcur < n_list ? next_valid(tcur + 1) : n_list;
+    }
   }
 
   // Epilogue: normalise, write out (bf16) and lse.
@@ -328,7 +354,7 @@ void prefill_kernel(PrefillArgs a) {
       }
     if (a.lse && h == 0)
       a.lse[(size_t)(b * a.Hq + hq) * L + row] =
-          l_tot > 0.f ? m_run * a.inv_sqrt_d + __logf(l_tot) : -INFINITY;
+          l_tot > 0.f ? m_ref * a.inv_sqrt_d + __logf(l_tot) : -INFINITY;
   }
   if (a.skip_counts && tid == 0) a.skip_counts[unit] = skipped;
 }
