@@ -15,7 +15,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libssa.so")
+# SSA_LIB may name another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("SSA_LIB") or os.path.join(_HERE, "libssa.so")
 
 SSA_OK = 0
 SSA_ERR_INVALID_ARG = -1

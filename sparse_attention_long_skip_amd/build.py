@@ -26,17 +26,22 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source to an object (in parallel) and link libssa.so.
-    Always rebuilds. Returns the library path."""
-    objdir = os.path.join(HERE, "_build")
+def build(verbose: bool = False, jobs: int = 4, lib_path: str = LIB, overrides: dict | None = None,
+          objdir: str | None = None) -> str:
+    """Compile every source to an object (in parallel) and link the library
+    (libssa.so in the package by default). ``overrides`` maps a source name
+    to another file to compile in its place. Always rebuilds. Returns the
+    library path."""
+    overrides = overrides or {}
+    objdir = objdir or os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     procs, objs = [], []
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        path = overrides.get(src, os.path.join(CSRC, src))
+        cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *lang, "-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
@@ -44,24 +49,24 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             procs[0][1].wait()
     failed = []
     for src, p in procs:
-        out, _ = p.communicate()
-        out = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
+        log, _ = p.communicate()
+        log = "\n".join(l for l in log.splitlines() if "packed-fp32-ops" not in l)
         if p.returncode != 0:
-            failed.append((src, out))
-        elif verbose and out.strip():
-            print(out)
+            failed.append((src, log))
+        elif verbose and log.strip():
+            print(log)
     if failed:
         msg = "\n".join(f"--- {s}\n{o}" for s, o in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
-    tmp = LIB + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

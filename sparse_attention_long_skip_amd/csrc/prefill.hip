@@ -75,7 +75,7 @@ __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 
 
 // STATS: write per-tile decisions / margins (a separate instance, so the hot
 // instance carries none of that code).
-template <int D, int BR, bool STATS>
+template <int D, int BR, bool STATS, bool SPARSE>
 __global__ __launch_bounds__(BR * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillArgs a) {
   constexpr int NW = BR / 32;
@@ -131,18 +131,18 @@ void prefill_kernel(PrefillArgs a) {
   // Visit list: dense (ascending tiles up to the causal limit) or a block list.
   const int32_t* list = nullptr;
   int n_list;
-  if (a.block_idx) {
+  if (SPARSE) {
     list = a.block_idx + unit * a.max_blocks;
     n_list = min(max(a.block_cnt[unit], 0), a.max_blocks);
   } else {
     n_list = a.causal ? (last_row / BC + 1) : a.nK;
   }
-  auto tile_of = [&](int t) -> int { return list ? list[t] : t; };
+  auto tile_of = [&](int t) -> int { return SPARSE ? list[t] : t; };
   auto valid = [&](int j) -> bool {
     return j >= 0 && j < a.nK && (!a.causal || j * BC <= last_row);
   };
   auto next_valid = [&](int t) -> int {
-    if (!list) return t;
+    if (!SPARSE) return t;
     while (t < n_list && !valid(list[t])) ++t;
     return t;
   };
@@ -363,10 +363,16 @@ template <int D, int BR>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)(a.per_xcd * kNumXcd));
   dim3 block(BR * 2);
-  if (a.tile_state || a.tile_margin)
-    hipLaunchKernelGGL((prefill_kernel<D, BR, true>), grid, block, 0, stream, a);
+  const bool stats = a.tile_state || a.tile_margin;
+  const bool sparse = a.block_idx != nullptr;
+  if (stats && sparse)
+    hipLaunchKernelGGL((prefill_kernel<D, BR, true, true>), grid, block, 0, stream, a);
+  else if (stats)
+    hipLaunchKernelGGL((prefill_kernel<D, BR, true, false>), grid, block, 0, stream, a);
+  else if (sparse)
+    hipLaunchKernelGGL((prefill_kernel<D, BR, false, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, BR, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BR, false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
