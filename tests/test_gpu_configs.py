@@ -1,0 +1,79 @@
+"""GPU parity at the full sizes of the five seeded workloads.
+
+The HIP path runs on the whole input, exactly as the benchmark times it; the
+oracle recomputes a seeded sample of decision units (always including the
+first and the last query tile of a head) plus, for the block mask, whole
+heads. Thresholds that target a skip ratio are calibrated on the oracle's own
+margins of the sampled units."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import prefill_parity, decode_parity, mask_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _units(rng, B, Hq, nQ, n):
+    u = {(0, 0, 0), (B - 1, Hq - 1, nQ - 1), (0, Hq // 2, nQ // 2)}
+    while len(u) < n:
+        u.add((int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(nQ))))
+    return sorted(u)
+
+
+def test_config1_gqa_16k_half_skipped():
+    c = synth.CONFIGS[1]
+    x = synth.prefill_inputs(1, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"], frac=c["frac"])
+    nQ = math.ceil(c["L"] / c["Br"])
+    units = _units(np.random.default_rng(11), c["B"], c["Hq"], nQ, 14)
+    m = oracle.prefill(x["q"], x["k"], x["v"], -math.inf, c["Br"], c["Bc"], True, units=units, bits=True)["margin"]
+    lam = oracle.lambda_for_ratio(m, c["target_skip"])
+    r = prefill_parity(x["q"], x["k"], x["v"], lam, c["Br"], c["Bc"], True, units=units)
+    print(f"config 1: lambda {lam:.4f}, sampled skip {r['skipped']}/{r['visited']}, exempt {r['exempt']}, "
+          f"max err {r['max_err_out']:.2e}, rel L2 {r['rel_l2_out']:.2e}")
+    assert 0.3 < r["skipped"] / r["visited"] < 0.7
+
+
+@pytest.mark.parametrize("lam", [-3.0, -9.0])
+def test_config3_128k_threshold_sweep_ends(lam):
+    c = synth.CONFIGS[3]
+    x = synth.prefill_inputs(3, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"], frac=c["frac"])
+    nQ = math.ceil(c["L"] / c["Br"])
+    units = _units(np.random.default_rng(12), c["B"], c["Hq"], nQ, 4)
+    r = prefill_parity(x["q"], x["k"], x["v"], lam, c["Br"], c["Bc"], True, units=units)
+    print(f"config 3 lambda {lam}: sampled skip {r['skipped']}/{r['visited']}, max err {r['max_err_out']:.2e}")
+
+
+def test_config2_decode_half_v_tiles_skipped():
+    c = synth.CONFIGS[2]
+    y = synth.decode_inputs(2, 0, c["B"], c["Hq"], c["Hkv"], c["S_max"], c["d"], c["len_lo"], c["len_hi"],
+                            block=c["Bc"], frac=c["frac"])
+    rng = np.random.default_rng(13)
+    units = sorted({(0, 0), (c["B"] - 1, c["Hkv"] - 1)} |
+                   {(int(rng.integers(c["B"])), int(rng.integers(c["Hkv"]))) for _ in range(6)})
+    m = oracle.decode(y["q"], y["k_cache"], y["v_cache"], y["seqlens"], -math.inf, c["Bc"], c["split_tiles"],
+                      units=units, bits=True)["margin"]
+    lam = oracle.lambda_for_ratio(m, c["target_skip"])
+    r = decode_parity(y, lam, c["split_tiles"], units=units)
+    print(f"config 2: lambda {lam:.4f}, sampled skip {r['skipped']}/{r['visited']}, exempt {r['exempt']}, "
+          f"max err {r['max_err_out']:.2e}")
+    assert 0.3 < r["skipped"] / r["visited"] < 0.7
+
+
+def test_config4_mask_and_block_sparse_prefill():
+    c = synth.CONFIGS[4]
+    x = synth.prefill_inputs(4, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"], frac=c["frac"])
+    mk = mask_parity(x["q"], x["k"], c["pool"], c["topk"], c["sink_blocks"], c["window_tokens"],
+                     heads=[(0, 0), (0, 9)])
+    print(f"config 4 mask: near-tie differences {mk['ties']}")
+    ref = oracle.block_mask(x["q"], x["k"], c["pool"], c["topk"], c["sink_blocks"], c["window_tokens"], bits=True)
+    nQ = math.ceil(c["L"] / c["Br"])
+    units = _units(np.random.default_rng(14), c["B"], c["Hq"], nQ, 10)
+    r = prefill_parity(x["q"], x["k"], x["v"], c["lam"], c["Br"], c["Bc"], True,
+                       block_idx=ref["block_idx"].astype(np.int32), block_cnt=ref["block_cnt"].astype(np.int32),
+                       units=units)
+    print(f"config 4 prefill: sampled skip {r['skipped']}/{r['visited']}, max err {r['max_err_out']:.2e}")
