@@ -253,6 +253,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only-main", action="store_true", help="skip extra and cpu baseline (profiling)")
+    ap.add_argument("--leg", choices=["prefill_128k", "decode", "block_sparse_32k"],
+                    help="run only this extra leg and print its JSON (profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the main leg, copy a 1 GiB buffer 5 times (HBM counter scale)")
     args = ap.parse_args()
@@ -269,6 +271,10 @@ def main():
 
     ssa.lib()
     torch.cuda.set_device(0)
+    legs = {"prefill_128k": extra_128k, "decode": extra_decode, "block_sparse_32k": extra_sparse}
+    if args.leg:
+        print(json.dumps({args.leg: legs[args.leg](args, torch, np, ssa, synth)}), flush=True)
+        return
     c = synth.CONFIGS[1]
     log("generating the 16K prefill workload")
     p = bench_prefill(1, args, torch, np, ssa, synth, target=c["target_skip"])
@@ -318,7 +324,7 @@ def main():
         del src, dst
     extra = {}
     if not (args.no_extra or args.only_main):
-        for name, fn in (("prefill_128k", extra_128k), ("decode", extra_decode), ("block_sparse_32k", extra_sparse)):
+        for name, fn in legs.items():
             try:
                 log(f"extra: {name}")
                 extra[name] = fn(args, torch, np, ssa, synth)
