@@ -12,10 +12,11 @@
 //
 // Kernels: (1) pool -- one workgroup per (block, head, batch, Q-or-K), a
 // single coalesced pass over Q and K (the HBM-bound part); (2) select -- one
-// workgroup per (query block, head, batch): scores into LDS as 64-bit sort
+// workgroup per (4 query blocks, head, batch): scores into LDS as 64-bit
 // keys (order-preserving float bits, then the inverted index so that equal
-// scores put the lower index first), a bitonic sort, flags for the kept
-// set, and an ordered compaction.
+// scores put the lower index first); then one wave per row finds the top-k
+// threshold by radix selection with ballot counts and compacts the kept set
+// in ascending order.
 #include "common.h"
 #include "launch.h"
 
@@ -31,7 +32,7 @@ struct MaskArgs {
   int32_t* block_idx;
   int32_t* block_cnt;
   float* block_scores;
-  int B, H, L, nB, pool, topk, sink, W, max_blocks;
+  int B, H, L, nB, nBp, pool, topk, sink, W, max_blocks;
   float inv_sqrt_d;
 };
 
@@ -75,95 +76,125 @@ __device__ __forceinline__ uint32_t order_bits(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int D>
+// One workgroup per (QPB consecutive query blocks, head, batch). Scores of
+// every causal candidate are turned into 64-bit keys (order-preserving float
+// bits, then the inverted index, so a larger key is a higher score or, on a
+// tie, a lower index). A candidate is in the top-k iff its key is at least
+// the topk-th largest key. The kept set is compacted in ascending order with
+// wave ballots.
+template <int D, int QPB>
 __global__ __launch_bounds__(256) void select_kernel(MaskArgs a) {
   constexpr int NT = 256;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ float qv[D];
-  __shared__ int seg_count[NT];
-  const int qb = blockIdx.x;
+  __shared__ float qv[QPB][D];
+  const int qb0 = blockIdx.x * QPB;
   const int hh = blockIdx.y;
   const int b = blockIdx.z;
   const int t = threadIdx.x;
-  const int N = qb + 1;  // causal candidates 0..qb
-  int Np = 1;
-  while (Np < N) Np <<= 1;
-  const int nBp = [&] { int x = 1; while (x < a.nB) x <<= 1; return x; }();
-  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);
-  unsigned char* flags = smem + (size_t)nBp * sizeof(uint64_t);
+  const int lane = t & 63;
+  const int wv = t >> 6;
+  const int nq = min(QPB, a.nB - qb0);
+  const int N_max = qb0 + nq;  // candidates 0 .. N_max - 1 cover every row here
+  const int nBp = a.nBp;
+  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);  // [QPB][nBp]
 
   const size_t hb = (size_t)b * a.H + hh;
-  if (t < D) qv[t] = a.qbar[(hb * a.nB + qb) * D + t];
+  for (int x = t; x < nq * D; x += NT) qv[x / D][x % D] = a.qbar[(hb * a.nB + qb0 + x / D) * D + x % D];
   __syncthreads();
 
+  // Scores: each pooled key row is read once for all QPB query blocks.
   const float* kb = a.kbar + hb * a.nB * D;
-  for (int c = t; c < Np; c += NT) {
-    uint64_t key = 0;
-    if (c < N) {
-      const float* kr = kb + (size_t)c * D;
-      float s = 0.f;
-#pragma unroll 8
-      for (int e = 0; e < D; e += 4) {
-        const f32x4 kx = *reinterpret_cast<const f32x4*>(kr + e);
-        s = fmaf(qv[e], kx[0], s);
-        s = fmaf(qv[e + 1], kx[1], s);
-        s = fmaf(qv[e + 2], kx[2], s);
-        s = fmaf(qv[e + 3], kx[3], s);
+  for (int c = t; c < N_max; c += NT) {
+    float acc[QPB];
+#pragma unroll
+    for (int q = 0; q < QPB; ++q) acc[q] = 0.f;
+    const float* kr = kb + (size_t)c * D;
+#pragma unroll 4
+    for (int e = 0; e < D; e += 4) {
+      const f32x4 kx = *reinterpret_cast<const f32x4*>(kr + e);
+#pragma unroll
+      for (int q = 0; q < QPB; ++q) {
+        acc[q] = fmaf(qv[q][e], kx[0], acc[q]);
+        acc[q] = fmaf(qv[q][e + 1], kx[1], acc[q]);
+        acc[q] = fmaf(qv[q][e + 2], kx[2], acc[q]);
+        acc[q] = fmaf(qv[q][e + 3], kx[3], acc[q]);
       }
-      s *= a.inv_sqrt_d;
-      if (a.block_scores) a.block_scores[(hb * a.nB + qb) * a.nB + c] = s;
-      key = ((uint64_t)order_bits(s) << 32) | (uint64_t)(0xffffffffu - (uint32_t)c);
     }
-    keys[c] = key;
-    if (c < N) flags[c] = 0;
+#pragma unroll
+    for (int q = 0; q < QPB; ++q) {
+      if (q >= nq) break;
+      const int qb = qb0 + q;
+      uint64_t key = 0;
+      if (c <= qb) {
+        const float sc = acc[q] * a.inv_sqrt_d;
+        if (a.block_scores) a.block_scores[(hb * a.nB + qb) * a.nB + c] = sc;
+        key = ((uint64_t)order_bits(sc) << 32) | (uint64_t)(0xffffffffu - (uint32_t)c);
+      }
+      keys[q * nBp + c] = key;
+    }
   }
   if (a.block_scores)
-    for (int c = N + t; c < a.nB; c += NT) a.block_scores[(hb * a.nB + qb) * a.nB + c] = -INFINITY;
+    for (int q = 0; q < nq; ++q)
+      for (int c = qb0 + q + 1 + t; c < a.nB; c += NT)
+        a.block_scores[(hb * a.nB + qb0 + q) * a.nB + c] = -INFINITY;
   __syncthreads();
 
-  // Bitonic sort, descending.
-  for (int kk = 2; kk <= Np; kk <<= 1) {
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int i = t; i < Np; i += NT) {
-        const int ixj = i ^ jj;
-        if (ixj > i) {
-          const uint64_t x = keys[i], y = keys[ixj];
-          const bool desc = (i & kk) == 0;
-          if (desc ? (x < y) : (x > y)) {
-            keys[i] = y;
-            keys[ixj] = x;
-          }
-        }
+  // Selection: wave wv owns row qb0 + wv (QPB == 4 rows per workgroup, or
+  // one row handled by wave 0). The top-k threshold is the topk-th largest
+  // key T: the largest value with #{key >= T} >= topk (keys are distinct,
+  // so exactly topk keys are >= T), found by a 64-round radix selection
+  // whose counts are wave ballots; no barriers.
+  constexpr int NREG = 8;  // rows with at most 512 candidates keep keys in registers
+  const int q = (QPB == 1) ? 0 : wv;
+  if ((QPB == 1 && wv != 0) || q >= nq) return;
+  const int qb = qb0 + q;
+  const int N = qb + 1;
+  const uint64_t* kq = keys + q * nBp;
+  const int nch = (N + 63) / 64;
+  uint64_t kr[NREG];
+  const bool in_reg = nch <= NREG;
+  if (in_reg) {
+#pragma unroll
+    for (int r = 0; r < NREG; ++r) kr[r] = (r * 64 + lane < N) ? kq[r * 64 + lane] : 0ull;
+  }
+  auto key_at = [&](int r) -> uint64_t {
+    if (in_reg) {
+      uint64_t v = 0;
+#pragma unroll
+      for (int rr = 0; rr < NREG; ++rr) v = (rr == r) ? kr[rr] : v;
+      return v;
+    }
+    const int c = r * 64 + lane;
+    return c < N ? kq[c] : 0ull;
+  };
+  uint64_t thr = 0;
+  const bool by_score = a.topk > 0 && a.topk < N;
+  if (by_score) {
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t cand = thr | (1ull << bit);
+      int cnt = 0;
+      if (in_reg) {
+#pragma unroll
+        for (int r = 0; r < NREG; ++r) cnt += __popcll(__ballot(kr[r] >= cand));
+      } else {
+        for (int r = 0; r < nch; ++r) cnt += __popcll(__ballot(key_at(r) >= cand));
       }
-      __syncthreads();
+      if (cnt >= a.topk) thr = cand;
     }
   }
-  const int ntop = min(a.topk, N);
-  for (int r = t; r < ntop; r += NT) flags[0xffffffffu - (uint32_t)(keys[r] & 0xffffffffu)] = 1;
-  for (int c = t; c < min(a.sink, N); c += NT) flags[c] = 1;
-  for (int c = max(0, N - a.W) + t; c < N; c += NT) flags[c] = 1;
-  __syncthreads();
-
-  // Ordered compaction: each thread owns a contiguous segment.
-  const int seg = (N + NT - 1) / NT;
-  const int c0 = min(N, t * seg), c1 = min(N, c0 + seg);
-  int cnt = 0;
-  for (int c = c0; c < c1; ++c) cnt += flags[c];
-  seg_count[t] = cnt;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    const int v = (t >= off) ? seg_count[t - off] : 0;
-    __syncthreads();
-    seg_count[t] += v;
-    __syncthreads();
-  }
-  const int total = seg_count[NT - 1];
-  int pos = seg_count[t] - cnt;
+  const bool all_top = a.topk >= N;
   int32_t* out = a.block_idx + (hb * a.nB + qb) * a.max_blocks;
-  for (int c = c0; c < c1; ++c)
-    if (flags[c]) out[pos++] = c;
-  for (int r = total + t; r < a.max_blocks; r += NT) out[r] = -1;
-  if (t == 0) a.block_cnt[hb * a.nB + qb] = total;
+  int base = 0;
+  for (int r = 0; r < nch; ++r) {
+    const int c = r * 64 + lane;
+    bool kept = false;
+    if (c < N) kept = (c < a.sink) || (c >= N - a.W) || all_top || (by_score && key_at(r) >= thr);
+    const uint64_t bal = __ballot(kept);
+    if (kept) out[base + __popcll(bal & ((1ull << lane) - 1ull))] = c;
+    base += __popcll(bal);
+  }
+  for (int r = base + lane; r < a.max_blocks; r += 64) out[r] = -1;
+  if (lane == 0) a.block_cnt[hb * a.nB + qb] = base;
 }
 
 template <int D>
@@ -171,10 +202,15 @@ hipError_t launch(const MaskArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((pool_kernel<D>), dim3(a.nB, a.H, a.B * 2), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int nBp = 1;
-  while (nBp < a.nB) nBp <<= 1;
-  const size_t shm = (size_t)nBp * (sizeof(uint64_t) + 1);
-  hipLaunchKernelGGL((select_kernel<D>), dim3(a.nB, a.H, a.B), dim3(256), shm, stream, a);
+  if (a.nB <= 1024) {
+    constexpr int QPB = 4;
+    const size_t shm = (size_t)QPB * a.nBp * sizeof(uint64_t);
+    hipLaunchKernelGGL((select_kernel<D, QPB>), dim3((a.nB + QPB - 1) / QPB, a.H, a.B), dim3(256), shm,
+                       stream, a);
+  } else {
+    const size_t shm = (size_t)a.nBp * sizeof(uint64_t);
+    hipLaunchKernelGGL((select_kernel<D, 1>), dim3(a.nB, a.H, a.B), dim3(256), shm, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -189,6 +225,7 @@ hipError_t launch_block_mask(const MaskParams& p, hipStream_t stream) {
   a.L = p.L;
   a.pool = p.pool;
   a.nB = (p.L + p.pool - 1) / p.pool;
+  a.nBp = a.nB;
   a.topk = p.topk;
   a.sink = p.sink_blocks;
   a.W = p.window_tokens > 0 ? (p.window_tokens + p.pool - 1) / p.pool : 0;

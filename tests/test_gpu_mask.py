@@ -28,3 +28,23 @@ def test_block_sparse_prefill_with_oracle_mask():
                            block_idx=m["block_idx"].astype(np.int32),
                            block_cnt=m["block_cnt"].astype(np.int32))
         print(f"lam={lam}: skipped {r['skipped']}/{r['visited']}")
+
+
+def test_mask_long_sequence_radix_path():
+    # nB = 1100 > 1024 exercises the one-row-per-workgroup instance
+    x = synth.prefill_inputs(402, 0, 1, 1, 1, 1100 * 64 - 17, 64)
+    r = mask_parity(x["q"], x["k"], 64, 64, 1, 1024)
+    print(f"near-tie differences {r['ties']}")
+
+
+def test_mask_ties_prefer_lower_index():
+    import torch
+    import sparse_attention_long_skip_amd as ssa
+    # identical rows everywhere: all pooled scores tie, so the top-k are the lowest indices
+    q = torch.ones((1, 1, 64 * 40, 64), dtype=torch.bfloat16, device="cuda")
+    k = torch.ones_like(q)
+    g = ssa.block_mask(q, k, 64, 5, 0, 0)
+    torch.cuda.synchronize()
+    idx, cnt = g["block_idx"].cpu().numpy(), g["block_cnt"].cpu().numpy()
+    for b in range(40):
+        assert idx[0, 0, b, :cnt[0, 0, b]].tolist() == list(range(min(5, b + 1)))
