@@ -34,10 +34,12 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(files=("common.h", "launch.h", "prefill.hip")) -> str:
+    """Hash of the sources the prefill kernel is built from (the counters in
+    profiles/ are valid only for this exact kernel)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_attention_long_skip_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

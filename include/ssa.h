@@ -89,6 +89,28 @@ int ssa_prefill(const void* q, const void* k, const void* v, void* out, float* l
                 int max_blocks, void* stream);
 
 /*
+ * ssa_prefill_nm -- ssa_prefill with N:M sparse softmax applied to the scores
+ * before the tile rule (Model Optimizer attention-sparsity tutorial, step 2:
+ * in every M consecutive key positions only the top-N scores are kept and
+ * the others set to -inf, a prefill-only method; its FAQ: keep sink tokens
+ * and a recent-token window dense).
+ *
+ * Same arguments as ssa_prefill (without a block list), plus:
+ *  nm_n, nm_m  keep the nm_n highest allowed scores in every aligned group of
+ *              nm_m keys (key c is in group c / nm_m; ties: lower key first).
+ *              nm_m in {2, 4}; 1 <= nm_n <= nm_m (nm_n == nm_m is dense).
+ *  dense_sink_tokens    keys c < this are always kept (>= 0).
+ *  dense_recent_tokens  keys with row - this < c <= row are always kept (>= 0).
+ * lambda = -INFINITY gives N:M sparse softmax alone; a finite lambda applies
+ * the Skip-Softmax rule to the N:M-masked scores.
+ */
+int ssa_prefill_nm(const void* q, const void* k, const void* v, void* out, float* lse,
+                   int32_t* skip_counts, uint8_t* tile_state, float* tile_margin,
+                   int B, int Hq, int Hkv, int L, int d, int Br, int Bc, float lambda,
+                   int causal, int nm_n, int nm_m, int dense_sink_tokens,
+                   int dense_recent_tokens, void* stream);
+
+/*
  * ssa_decode_workspace_size -- bytes of device workspace ssa_decode needs:
  * per (sequence, query head, split) one fp32 partial output of d values plus
  * its running max and row-sum. Returns 0 for invalid sizes.

@@ -97,14 +97,44 @@ def _softmax_out(s_list, v_list, nrows, d):
     return o, lse, m, l, p
 
 
+def nm_mask(s: np.ndarray, rows: np.ndarray, cols: np.ndarray, n: int, m: int,
+            dense_sink: int = 0, dense_recent: int = 0) -> np.ndarray:
+    """N:M sparse softmax mask (Model Optimizer tutorial, step 2: in every M
+    consecutive key positions only the top-N scores are kept, the others are
+    set to -inf; FAQ: sink tokens and recent tokens stay dense).
+
+    s [nrows, ncols] holds scores with -inf where not allowed; rows/cols are
+    the absolute positions. Groups are aligned: key c is in group c // m.
+    Within a group, allowed positions are ranked by score (ties: lower c
+    first) and the top n are kept; positions c < dense_sink or
+    row - dense_recent < c <= row are kept as well. Returns the masked copy."""
+    out = np.full_like(s, -np.inf)
+    for a, r in enumerate(rows):
+        for g0 in range(0, s.shape[1], m):
+            idx = list(range(g0, min(g0 + m, s.shape[1])))
+            allowed = [i for i in idx if s[a, i] > -np.inf]
+            ranked = sorted(allowed, key=lambda i: (-s[a, i], cols[i]))
+            keep = set(ranked[:n])
+            for i in allowed:
+                c = cols[i]
+                if c < dense_sink or r - dense_recent < c <= r:
+                    keep.add(i)
+            for i in keep:
+                out[a, i] = s[a, i]
+    return out
+
+
 def prefill(q, k, v, lam: float, Br: int, Bc: int, causal: bool = True,
             block_idx=None, block_cnt=None, units=None, forced=None,
-            bits: bool = False, return_probs: bool = False) -> dict:
+            bits: bool = False, return_probs: bool = False, nm=None,
+            dense_sink: int = 0, dense_recent: int = 0) -> dict:
     """Skip-Softmax prefill. q [B,Hq,L,d]; k, v [B,Hkv,L,d]; query head hq
     reads KV head hq // (Hq/Hkv).
 
     ``block_idx`` [B,Hq,nQ,max] / ``block_cnt`` [B,Hq,nQ] restrict each query
-    tile to a list of key tiles. ``units`` limits the work to a list of
+    tile to a list of key tiles. ``nm`` = (N, M) applies N:M sparse softmax
+    (``nm_mask``, with ``dense_sink`` / ``dense_recent`` exemptions) to the
+    scores before the tile rule. ``units`` limits the work to a list of
     (b, hq, i). ``forced`` [B,Hq,nQ,nK] (KEPT/SKIPPED) replaces the rule's
     decisions (replay). Returns a dict with out [B,Hq,L,d], lse [B,Hq,L],
     decision and margin [B,Hq,nQ,nK] (margin NaN where not visited),
@@ -140,6 +170,8 @@ def prefill(q, k, v, lam: float, Br: int, Bc: int, causal: bool = True,
                 s = (qi @ _widen(k[b, kvh, c0:c1], bits).T) * scale
                 if causal:
                     s[np.arange(c0, c1)[None, :] > rows[:, None]] = -np.inf
+                if nm is not None:
+                    s = nm_mask(s, rows, np.arange(c0, c1), nm[0], nm[1], dense_sink, dense_recent)
                 m_loc = s.max(axis=1)
                 g = _row_gaps(m_loc, m_prev).max()
                 margin[b, hq, i, j] = g

@@ -131,3 +131,27 @@ def topk_blocks(q, k, pool, topk, sink_blocks, window_tokens):
         keep |= {c for c in range(max(0, b - W + 1), b + 1)}
         res.append(sorted(keep))
     return res
+
+
+def nm_attention(q, k, v, n, m, causal, dense_sink=0, dense_recent=0):
+    """One head, N:M sparse softmax without tile skipping, by explicit loops:
+    for each row and each aligned group of m keys, keep the n allowed keys
+    with the highest scores (ties: lower index), plus sink / recent keys."""
+    L, d = len(q), len(q[0])
+    out, lses = [], []
+    for r in range(L):
+        kept = []
+        for g0 in range(0, L, m):
+            grp = [c for c in range(g0, min(g0 + m, L)) if not (causal and c > r)]
+            sc = [(-_dot(q[r], k[c]) / math.sqrt(d), c) for c in grp]
+            sc.sort()
+            chosen = {c for _, c in sc[:n]}
+            chosen |= {c for c in grp if c < dense_sink or r - dense_recent < c <= r}
+            kept.extend(sorted(chosen))
+        s = [_dot(q[r], k[c]) / math.sqrt(d) for c in kept]
+        mx = max(s)
+        w = [math.exp(x - mx) for x in s]
+        tot = sum(w)
+        out.append([sum(w[t] * float(v[c][e]) for t, c in enumerate(kept)) / tot for e in range(len(v[0]))])
+        lses.append(mx + math.log(tot))
+    return out, lses

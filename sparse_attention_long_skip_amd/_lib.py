@@ -35,6 +35,7 @@ _sz = ctypes.c_size_t
 
 _SIGNATURES = {
     "ssa_prefill": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _p, _p, _i, _p]),
+    "ssa_prefill_nm": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _i, _i, _p]),
     "ssa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "ssa_decode": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _sz, _p]),
     "ssa_block_mask_max_blocks": (_i, [_i, _i, _i, _i, _i]),
@@ -111,10 +112,12 @@ def _check(fn, status):
 
 def prefill(q, k, v, lam: float, Br: int = 128, Bc: int = 64, causal: bool = True,
             block_idx=None, block_cnt=None, lse: bool = True, stats: bool = False,
-            margins: bool = False, out=None, stream=None) -> dict:
-    """Skip-Softmax prefill (``ssa_prefill``). q [B,Hq,L,d], k/v [B,Hkv,L,d]
-    bf16. Returns a dict: out, and lse / skip_counts / tile_state /
-    tile_margin as requested (tile arrays are zero / NaN where not visited)."""
+            margins: bool = False, out=None, stream=None, nm=None, dense_sink: int = 0,
+            dense_recent: int = 0) -> dict:
+    """Skip-Softmax prefill (``ssa_prefill``; ``ssa_prefill_nm`` when ``nm`` =
+    (N, M) asks for N:M sparse softmax). q [B,Hq,L,d], k/v [B,Hkv,L,d] bf16.
+    Returns a dict: out, and lse / skip_counts / tile_state / tile_margin as
+    requested (tile arrays are zero / NaN where not visited)."""
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
     _need(v, "v", torch.bfloat16, 4)
@@ -134,6 +137,16 @@ def prefill(q, k, v, lam: float, Br: int = 128, Bc: int = 64, causal: bool = Tru
         _need(block_idx, "block_idx", torch.int32, 4)
         _need(block_cnt, "block_cnt", torch.int32, 3)
         max_blocks = block_idx.shape[3]
+    if nm is not None:
+        if block_idx is not None:
+            raise ValueError("N:M sparse softmax does not take a block list")
+        st = lib().ssa_prefill_nm(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(res["out"]), _ptr(res["lse"]), _ptr(res["skip_counts"]),
+            _ptr(res["tile_state"]), _ptr(res["tile_margin"]), B, Hq, Hkv, L, d, Br, Bc, float(lam),
+            int(bool(causal)), int(nm[0]), int(nm[1]), int(dense_sink), int(dense_recent),
+            _stream(stream))
+        _check("ssa_prefill_nm", st)
+        return res
     st = lib().ssa_prefill(
         _ptr(q), _ptr(k), _ptr(v), _ptr(res["out"]), _ptr(res["lse"]), _ptr(res["skip_counts"]),
         _ptr(res["tile_state"]), _ptr(res["tile_margin"]), B, Hq, Hkv, L, d, Br, Bc, float(lam),

@@ -23,6 +23,7 @@ struct PrefillParams {
   const int32_t* block_idx;
   const int32_t* block_cnt;
   int max_blocks;
+  int nm_n = 0, nm_m = 0, dense_sink = 0, dense_recent = 0;  // N:M sparse softmax (0: off)
 };
 
 struct DecodeParams {

@@ -64,6 +64,7 @@ struct PrefillArgs {
   const int32_t* block_idx;
   const int32_t* block_cnt;
   int max_blocks;
+  int nm_n, nm_m, dense_sink, dense_recent;  // N:M sparse softmax (NM instances)
 };
 
 // 16-byte chunk swizzles of a tile row (physical chunk = logical ^ swz(row)).
@@ -74,8 +75,9 @@ template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 // STATS: write per-tile decisions / margins (a separate instance, so the hot
-// instance carries none of that code).
-template <int D, int BR, bool STATS, bool SPARSE>
+// instance carries none of that code). SPARSE: visit a per-tile block list.
+// NM: N:M sparse softmax on the scores before the tile rule.
+template <int D, int BR, bool STATS, bool SPARSE, bool NM>
 __global__ __launch_bounds__(BR * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillArgs a) {
   constexpr int NW = BR / 32;
@@ -219,6 +221,47 @@ void prefill_kernel(PrefillArgs a) {
   // Pipeline over list positions t = 0 .. n+1, one barrier each:
   //   vote of tile t-1 -> issue V(t-1); issue K(t+1); P.V of tile t-2;
   //   exp of tile t-1; scores, row max and wave flag of tile t.
+  // N:M sparse softmax (Model Optimizer tutorial, step 2; FAQ on sink and
+  // recent tokens): in every aligned group of M consecutive keys a row keeps
+  // its top-N allowed scores (ties: lower key), plus keys below dense_sink
+  // and keys in (row - dense_recent, row]; the rest become -inf. A lane
+  // holds, per 8-key block, 4 consecutive keys (8q + 4h + 0..3), so groups
+  // of 2 or 4 are lane-local.
+  auto nm_sparsify = [&](int kbase) {
+    const bool exempt_here = (kbase < a.dense_sink) ||
+        (a.dense_recent > 0 && kbase + BC - 1 > q0 + w * 32 - a.dense_recent);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = s[kb][q4 * 4 + e];
+        bool keep[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int g0 = (a.nm_m == 2) ? (e & 2) : 0;
+          int rank = 0;
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            const bool same = (a.nm_m == 2) ? ((f & 2) == g0) : true;
+            if (f != e && same) rank += (x[f] > x[e] || (x[f] == x[e] && f < e)) ? 1 : 0;
+          }
+          keep[e] = rank < a.nm_n;
+        }
+        if (exempt_here) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = kbase + kb * 32 + q4 * 8 + h * 4 + e;
+            keep[e] = keep[e] || key < a.dense_sink || (row - a.dense_recent < key && key <= row);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (!keep[e]) s[kb][q4 * 4 + e] = -INFINITY;
+      }
+  };
+
   int tcur = next_valid(0);
   if (tcur < n_list) load_tile(kp, tile_of(tcur), k_lds[0], koff);
   int tnext = tcur < n_list ? next_valid(tcur + 1) : n_list;
@@ -314,6 +357,7 @@ void prefill_kernel(PrefillArgs a) {
             if (key >= L || (a.causal && key > row)) s[kb][e] = -INFINITY;
           }
       }
+      if (NM) nm_sparsify(kbase);
       float mloc = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -365,14 +409,19 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   dim3 block(BR * 2);
   const bool stats = a.tile_state || a.tile_margin;
   const bool sparse = a.block_idx != nullptr;
-  if (stats && sparse)
-    hipLaunchKernelGGL((prefill_kernel<D, BR, true, true>), grid, block, 0, stream, a);
+  const bool nm = a.nm_m > 0 && a.nm_n < a.nm_m;
+  if (nm && stats)
+    hipLaunchKernelGGL((prefill_kernel<D, BR, true, false, true>), grid, block, 0, stream, a);
+  else if (nm)
+    hipLaunchKernelGGL((prefill_kernel<D, BR, false, false, true>), grid, block, 0, stream, a);
+  else if (stats && sparse)
+    hipLaunchKernelGGL((prefill_kernel<D, BR, true, true, false>), grid, block, 0, stream, a);
   else if (stats)
-    hipLaunchKernelGGL((prefill_kernel<D, BR, true, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BR, true, false, false>), grid, block, 0, stream, a);
   else if (sparse)
-    hipLaunchKernelGGL((prefill_kernel<D, BR, false, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BR, false, true, false>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, BR, false, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BR, false, false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -405,6 +454,10 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   a.block_idx = p.block_idx;
   a.block_cnt = p.block_cnt;
   a.max_blocks = p.max_blocks;
+  a.nm_n = p.nm_n;
+  a.nm_m = p.nm_m;
+  a.dense_sink = p.dense_sink;
+  a.dense_recent = p.dense_recent;
   if (p.d == 128 && p.Br == 128) return launch<128, 128>(a, stream);
   if (p.d == 128 && p.Br == 64) return launch<128, 64>(a, stream);
   if (p.d == 64 && p.Br == 128) return launch<64, 128>(a, stream);

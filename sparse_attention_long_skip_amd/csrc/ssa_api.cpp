@@ -143,6 +143,44 @@ int ssa_prefill(const void* q, const void* k, const void* v, void* out, float* l
   return hip_status(ssa::launch_prefill(p, static_cast<hipStream_t>(stream)));
 }
 
+int ssa_prefill_nm(const void* q, const void* k, const void* v, void* out, float* lse,
+                   int32_t* skip_counts, uint8_t* tile_state, float* tile_margin, int B, int Hq,
+                   int Hkv, int L, int d, int Br, int Bc, float lambda, int causal, int nm_n, int nm_m,
+                   int dense_sink_tokens, int dense_recent_tokens, void* stream) {
+  const int st = check_prefill(q, k, v, out, B, Hq, Hkv, L, d, Br, Bc, lambda, causal, nullptr,
+                               nullptr, 0);
+  if (st != SSA_OK) return st;
+  if (nm_m <= 0 || nm_n <= 0 || nm_n > nm_m || dense_sink_tokens < 0 || dense_recent_tokens < 0)
+    return SSA_ERR_INVALID_ARG;
+  if (nm_m != 2 && nm_m != 4) return SSA_ERR_UNSUPPORTED;
+  ssa::PrefillParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.skip_counts = skip_counts;
+  p.tile_state = tile_state;
+  p.tile_margin = tile_margin;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.L = L;
+  p.d = d;
+  p.Br = Br;
+  p.Bc = Bc;
+  p.lambda = lambda;
+  p.causal = causal;
+  p.block_idx = nullptr;
+  p.block_cnt = nullptr;
+  p.max_blocks = 0;
+  p.nm_n = nm_n;
+  p.nm_m = nm_m;
+  p.dense_sink = dense_sink_tokens;
+  p.dense_recent = dense_recent_tokens;
+  return hip_status(ssa::launch_prefill(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t ssa_decode_workspace_size(int B, int Hq, int S_max, int d, int Bc, int split_tiles) {
   if (B <= 0 || Hq <= 0 || S_max <= 0 || d <= 0 || Bc <= 0 || split_tiles <= 0) return 0;
   return ssa::decode_workspace_bytes(B, Hq, S_max, d, Bc, split_tiles);

@@ -71,7 +71,7 @@ def compare_decisions(gpu_state, ref_decision, ref_margin, lam, band=BAND):
 
 
 def prefill_parity(q_bits, k_bits, v_bits, lam, Br, Bc, causal, block_idx=None, block_cnt=None,
-                   units=None, margins_atol=1e-3):
+                   units=None, margins_atol=1e-3, nm=None, dense_sink=0, dense_recent=0):
     """Run the HIP prefill on the whole input and the oracle on ``units``
     (all if None); compare. Returns a summary dict."""
     import sparse_attention_long_skip_amd as ssa
@@ -81,10 +81,12 @@ def prefill_parity(q_bits, k_bits, v_bits, lam, Br, Bc, causal, block_idx=None, 
         bi = torch.from_numpy(np.ascontiguousarray(block_idx, np.int32)).cuda()
         bc = torch.from_numpy(np.ascontiguousarray(block_cnt, np.int32)).cuda()
     g = ssa.prefill(q, k, v, lam, Br=Br, Bc=Bc, causal=causal, block_idx=bi, block_cnt=bc,
-                    lse=True, stats=True, margins=True)
+                    lse=True, stats=True, margins=True, nm=nm, dense_sink=dense_sink,
+                    dense_recent=dense_recent)
     torch.cuda.synchronize()
     ref = oracle.prefill(q_bits, k_bits, v_bits, lam, Br, Bc, causal, block_idx=block_idx,
-                         block_cnt=block_cnt, units=units, bits=True)
+                         block_cnt=block_cnt, units=units, bits=True, nm=nm,
+                         dense_sink=dense_sink, dense_recent=dense_recent)
     state = to_np(g["tile_state"])
     margin = to_np(g["tile_margin"])
     B, Hq, L, d = q_bits.shape
@@ -111,7 +113,8 @@ def prefill_parity(q_bits, k_bits, v_bits, lam, Br, Bc, causal, block_idx=None, 
     if replay_units:
         forced = state.astype(np.int8)
         rep = oracle.replay(q_bits, k_bits, v_bits, forced, Br, Bc, causal, block_idx=block_idx,
-                            block_cnt=block_cnt, units=replay_units, bits=True)
+                            block_cnt=block_cnt, units=replay_units, bits=True, nm=nm,
+                            dense_sink=dense_sink, dense_recent=dense_recent)
     got_o, ref_o, got_l, ref_l = [], [], [], []
     rs = set(replay_units)
     for (b, h, i) in units:

@@ -113,3 +113,16 @@ def test_mask_validation(lib):
     assert _mask(lib, L=64 * 5000, mb=81) == -2
     assert _mask(lib, ws=None) == -3
     assert _mask(lib, wsb=100) == -3
+
+
+def test_prefill_nm_validation(lib):
+    def call(n, m, sink=0, recent=0, d=128):
+        return lib.ssa_prefill_nm(FAKE, FAKE, FAKE, FAKE, None, None, None, None, 1, 2, 1, 128, d, 128, 64,
+                                  ctypes.c_float(-1.0), 1, n, m, sink, recent, None)
+    assert call(0, 4) == -1
+    assert call(5, 4) == -1
+    assert call(2, 4, sink=-1) == -1
+    assert call(2, 4, recent=-3) == -1
+    assert call(2, 8) == -2
+    assert call(1, 3) == -2
+    assert call(2, 4, d=96) == -2

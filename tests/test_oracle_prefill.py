@@ -267,3 +267,33 @@ def test_strict_comparison_keeps_exact_ties_at_zero():
     assert res["decision"][0, 0, 0, 1] == KEPT
     res = oracle.prefill(q, k, v, 1e-300, 4, 2, False)
     assert res["decision"][0, 0, 0, 1] == SKIPPED
+
+
+def test_nm_sparse_softmax_matches_bruteforce():
+    for seed in range(60):
+        rng, q, k, v = _case(seed, L=int(np.random.default_rng(seed).integers(2, 14)))
+        m = int(rng.choice([2, 4]))
+        n = int(rng.integers(1, m))
+        causal = bool(seed % 2)
+        sink = int(rng.integers(0, 3))
+        recent = int(rng.integers(0, 4))
+        res = oracle.prefill(q, k, v, -np.inf, 4, 4, causal, nm=(n, m), dense_sink=sink, dense_recent=recent)
+        o_ref, lse_ref = bruteforce.nm_attention(q[0, 0], k[0, 0], v[0, 0], n, m, causal, sink, recent)
+        np.testing.assert_allclose(res["out"][0, 0], np.array(o_ref), atol=1e-12)
+        np.testing.assert_allclose(res["lse"][0, 0], np.array(lse_ref), atol=1e-12)
+
+
+def test_nm_keeps_at_most_n_per_group_and_n_equal_m_is_dense():
+    rng, q, k, v = _case(3, L=16, d=4)
+    res = oracle.prefill(q, k, v, -np.inf, 4, 8, False, nm=(2, 4), return_probs=True)
+    P = res["probs"][0, 0]
+    for r in range(16):
+        for g0 in range(0, 16, 4):
+            assert np.count_nonzero(P[r, g0:g0 + 4]) == 2
+    a = oracle.prefill(q, k, v, -1.0, 4, 8, True, nm=(4, 4))
+    b = oracle.prefill(q, k, v, -1.0, 4, 8, True)
+    np.testing.assert_array_equal(a["out"], b["out"])
+    # exemptions covering every key give dense attention
+    c = oracle.prefill(q, k, v, -np.inf, 4, 8, True, nm=(1, 4), dense_recent=16)
+    d = oracle.prefill(q, k, v, -np.inf, 4, 8, True)
+    np.testing.assert_allclose(c["out"], d["out"], atol=1e-14)
