@@ -247,6 +247,30 @@ def extra_sparse(args, torch, np, ssa, synth):
             "mfma_frac_executed": round(ex / (ev_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def extra_nm(args, torch, np, ssa, synth):
+    """N:M (2:4) sparse softmax on the 16K GQA shape, alone and with ~50% tile skipping."""
+    from sparse_attention_long_skip_amd.calibrate import lambda_for_ratio
+    c = synth.CONFIGS[1]
+    x = synth.prefill_inputs(1, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"], frac=c["frac"])
+    q, k, v = (dev_bf16(x[n], torch, np) for n in ("q", "k", "v"))
+    del x
+    kw = dict(Br=c["Br"], Bc=c["Bc"], causal=True, nm=(2, 4), dense_sink=64, dense_recent=256)
+    m = ssa.prefill(q, k, v, -math.inf, margins=True, lse=False, **kw)["tile_margin"].cpu().numpy()
+    rows = []
+    out = torch.empty_like(q)
+    for lam in (-math.inf, lambda_for_ratio(m, 0.5)):
+        st = ssa.prefill(q, k, v, lam, stats=True, **kw)
+        torch.cuda.synchronize()
+        s = st["tile_state"].cpu().numpy()
+        vis, kept = int((s != 0).sum()), int((s == 1).sum())
+        ms, ev = time_launches(lambda: ssa.prefill(q, k, v, lam, out=out, **kw), 10, 3, torch)
+        rows.append({"lambda": None if lam == -math.inf else round(lam, 5), "ms": round(ms, 4),
+                     "skip_pct": round(100.0 * (vis - kept) / vis, 3),
+                     "dense_equiv_tflops": round(dense_flops(c) / ms / 1e9, 1),
+                     "mfma_frac_executed": round(2.0 * 128 * 64 * 128 * (vis + kept) / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
+    return {"workload": "N:M 2:4 sparse softmax, 16K GQA shape, dense sink 64 + recent 256 tokens", "runs": rows}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,7 +279,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only-main", action="store_true", help="skip extra and cpu baseline (profiling)")
-    ap.add_argument("--leg", choices=["prefill_128k", "decode", "block_sparse_32k"],
+    ap.add_argument("--leg", choices=["prefill_128k", "decode", "block_sparse_32k", "nm_2of4_16k"],
                     help="run only this extra leg and print its JSON (profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the main leg, copy a 1 GiB buffer 5 times (HBM counter scale)")
@@ -273,7 +297,8 @@ def main():
 
     ssa.lib()
     torch.cuda.set_device(0)
-    legs = {"prefill_128k": extra_128k, "decode": extra_decode, "block_sparse_32k": extra_sparse}
+    legs = {"prefill_128k": extra_128k, "decode": extra_decode, "block_sparse_32k": extra_sparse,
+            "nm_2of4_16k": extra_nm}
     if args.leg:
         print(json.dumps({args.leg: legs[args.leg](args, torch, np, ssa, synth)}), flush=True)
         return
