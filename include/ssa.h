@@ -71,8 +71,11 @@ extern "C" {
  *           log units, may be +-inf) of each visited tile; others untouched.
  *           Margins do not depend on lambda, so one call yields the skip
  *           ratio of every threshold.
- *  d in {64, 128}; Br in {64, 128}; Bc = 64. causal: key c is allowed for
- *  row r iff c <= r (L_q = L_k).
+ *  d in {64, 128}; Br in {32, 64, 128}; Bc = 64. causal: key c is allowed
+ *  for row r iff c <= r (L_q = L_k). Br is the decision unit: Br = 32 is the
+ *  warp-granular variant of the SpargeAttn page (stage two, "sparse warp
+ *  online softmax"): every 32-row group decides alone, while 128-row
+ *  workgroups share the K and V tiles (block lists need Br >= 64).
  *  lambda   <= 0 or -INFINITY; NaN or > 0 is rejected.
  *  block_idx [B, Hq, nQ, max_blocks] int32, nullable: for query tile i the
  *           first block_cnt[b,h,i] entries are the key tiles to visit, in

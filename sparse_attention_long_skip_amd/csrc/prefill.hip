@@ -8,7 +8,10 @@
 // Design:
 //  * One workgroup per (batch, query head, query tile of BR rows); BR/32
 //    waves, each owning 32 query rows; two workgroups per CU so that one
-//    workgroup's exponentials overlap the other's matrix work.
+//    workgroup's exponentials overlap the other's matrix work. The decision
+//    unit is the whole query tile, or, with Br = 32, each wave (SpargeAttn's
+//    warp-granular variant): then a wave skips its own exponentials and P.V,
+//    and the shared V tile is loaded when any wave keeps it.
 //  * Scores are computed transposed, S^T = K Q^T, with 32x32x16 bf16 MFMA:
 //    K rows come from LDS (A operand), Q stays in registers (B operand). The
 //    accumulator then gives every lane ONE query row (lane % 32) and 16 keys
@@ -65,6 +68,8 @@ struct PrefillArgs {
   const int32_t* block_cnt;
   int max_blocks;
   int nm_n, nm_m, dense_sink, dense_recent;  // N:M sparse softmax (NM instances)
+  int wave_vote;  // 1: every 32-row wave is its own decision unit (Br = 32)
+  int nQ_unit;    // decision units per (batch, head): nQ, or nQ * NW with wave_vote
 };
 
 // 16-byte chunk swizzles of a tile row (physical chunk = logical ^ swz(row)).
@@ -76,8 +81,9 @@ __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 
 
 // STATS: write per-tile decisions / margins (a separate instance, so the hot
 // instance carries none of that code). SPARSE: visit a per-tile block list.
-// NM: N:M sparse softmax on the scores before the tile rule.
-template <int D, int BR, bool STATS, bool SPARSE, bool NM>
+// NM: N:M sparse softmax on the scores before the tile rule. WV: per-wave
+// decision units (Br = 32).
+template <int D, int BR, bool STATS, bool SPARSE, bool NM, bool WV>
 __global__ __launch_bounds__(BR * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_kernel(PrefillArgs a) {
   constexpr int NW = BR / 32;
@@ -115,6 +121,10 @@ void prefill_kernel(PrefillArgs a) {
   const int row = q0 + w * 32 + r32;
   const bool row_ok = row < L;
   const int last_row = min(q0 + BR, L) - 1;
+  // This wave's rows: a tile none of them can see contributes nothing to
+  // them, so the wave skips its exponentials and P.V there.
+  const bool wave_rows = q0 + w * 32 < L;
+  const int wave_last = min(q0 + w * 32 + 31, L - 1);
 
   const uint16_t* qp = a.q + ((size_t)(b * a.Hq + hq) * L) * D;
   const uint16_t* kp = a.k + ((size_t)(b * a.Hkv + kvh) * L) * D;
@@ -274,26 +284,44 @@ void prefill_kernel(PrefillArgs a) {
     const int buf = it & 1;
     wait_vmem();
     __syncthreads();
-    bool keep1 = false;
+    bool keep1 = false;  // this wave takes the exponentials and P.V of tile jprev
     if (have_prev) {
+      // keep_any: some decision unit of the workgroup keeps the tile (V is
+      // loaded); keep_mine: this wave's unit keeps it.
+      bool keep_any, keep_mine;
+      const bool wvis = !WV || (wave_rows && (!a.causal || jprev * BC <= wave_last));
       if (STATS) {
         float g = flag_lds[buf ^ 1][0];
 #pragma unroll
         for (int ww = 1; ww < NW; ++ww) g = fmaxf(g, flag_lds[buf ^ 1][ww]);
-        keep1 = !(g < a.lam_raw);
-        if (tid == 0) {
+        keep_any = !(g < a.lam_raw);
+        const float gw = flag_lds[buf ^ 1][w];
+        keep_mine = WV ? !(gw < a.lam_raw) : keep_any;
+        if (WV) {
+          if (lane == 0 && wvis) {
+            const size_t ti = (((size_t)(b * a.Hq + hq) * a.nQ_unit) + i * NW + w) * a.nK + jprev;
+            if (a.tile_state) a.tile_state[ti] = keep_mine ? 1 : 2;
+            if (a.tile_margin) a.tile_margin[ti] = gw * a.inv_sqrt_d;
+          }
+        } else if (tid == 0) {
           const size_t ti = unit * a.nK + jprev;
-          if (a.tile_state) a.tile_state[ti] = keep1 ? 1 : 2;
+          if (a.tile_state) a.tile_state[ti] = keep_any ? 1 : 2;
           if (a.tile_margin) a.tile_margin[ti] = g * a.inv_sqrt_d;
         }
       } else {
         float f = flag_lds[buf ^ 1][0];
 #pragma unroll
         for (int ww = 1; ww < NW; ++ww) f += flag_lds[buf ^ 1][ww];
-        keep1 = f > 0.f;
+        keep_any = f > 0.f;
+        keep_mine = WV ? (flag_lds[buf ^ 1][w] > 0.f) : keep_any;
       }
-      if (keep1) load_tile(vp, jprev, v_lds[buf ^ 1], voff);
-      else ++skipped;
+      if (keep_any) load_tile(vp, jprev, v_lds[buf ^ 1], voff);
+      if (WV) {
+        if (wvis && !keep_mine) ++skipped;
+      } else if (!keep_any) {
+        ++skipped;
+      }
+      keep1 = WV ? (keep_mine && wvis) : keep_any;
     }
     if (tnext < n_list) load_tile(kp, tile_of(tnext), k_lds[buf ^ 1], koff);
     if (keep2) pv(buf);
@@ -400,7 +428,13 @@ void prefill_kernel(PrefillArgs a) {
       a.lse[(size_t)(b * a.Hq + hq) * L + row] =
           l_tot > 0.f ? m_ref * a.inv_sqrt_d + __logf(l_tot) : -INFINITY;
   }
-  if (a.skip_counts && tid == 0) a.skip_counts[unit] = skipped;
+  if (a.skip_counts) {
+    if (WV) {
+      if (lane == 0 && wave_rows) a.skip_counts[((size_t)(b * a.Hq + hq) * a.nQ_unit) + i * NW + w] = skipped;
+    } else if (tid == 0) {
+      a.skip_counts[unit] = skipped;
+    }
+  }
 }
 
 template <int D, int BR>
@@ -410,18 +444,24 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   const bool stats = a.tile_state || a.tile_margin;
   const bool sparse = a.block_idx != nullptr;
   const bool nm = a.nm_m > 0 && a.nm_n < a.nm_m;
-  if (nm && stats)
-    hipLaunchKernelGGL((prefill_kernel<D, BR, true, false, true>), grid, block, 0, stream, a);
-  else if (nm)
-    hipLaunchKernelGGL((prefill_kernel<D, BR, false, false, true>), grid, block, 0, stream, a);
-  else if (stats && sparse)
-    hipLaunchKernelGGL((prefill_kernel<D, BR, true, true, false>), grid, block, 0, stream, a);
-  else if (stats)
-    hipLaunchKernelGGL((prefill_kernel<D, BR, true, false, false>), grid, block, 0, stream, a);
-  else if (sparse)
-    hipLaunchKernelGGL((prefill_kernel<D, BR, false, true, false>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<D, BR, false, false, false>), grid, block, 0, stream, a);
+  const bool wv = a.wave_vote != 0;
+#define SSA_LAUNCH(ST, SP, NMF, WVF) \
+  hipLaunchKernelGGL((prefill_kernel<D, BR, ST, SP, NMF, WVF>), grid, block, 0, stream, a)
+  if (sparse) {
+    if (stats) SSA_LAUNCH(true, true, false, false);
+    else SSA_LAUNCH(false, true, false, false);
+  } else if (nm) {
+    if (stats && wv) SSA_LAUNCH(true, false, true, true);
+    else if (stats) SSA_LAUNCH(true, false, true, false);
+    else if (wv) SSA_LAUNCH(false, false, true, true);
+    else SSA_LAUNCH(false, false, true, false);
+  } else {
+    if (stats && wv) SSA_LAUNCH(true, false, false, true);
+    else if (stats) SSA_LAUNCH(true, false, false, false);
+    else if (wv) SSA_LAUNCH(false, false, false, true);
+    else SSA_LAUNCH(false, false, false, false);
+  }
+#undef SSA_LAUNCH
   return hipGetLastError();
 }
 
@@ -441,7 +481,10 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.L = p.L;
-  a.nQ = (p.L + p.Br - 1) / p.Br;
+  const int br_wg = p.Br == 32 ? 128 : p.Br;  // Br = 32: 128-row workgroups, per-wave votes
+  a.nQ = (p.L + br_wg - 1) / br_wg;
+  a.wave_vote = p.Br == 32 ? 1 : 0;
+  a.nQ_unit = (p.L + p.Br - 1) / p.Br;
   a.nK = (p.L + p.Bc - 1) / p.Bc;
   a.G = p.Hq / p.Hkv;
   a.tasks = p.B * p.Hq * a.nQ;
@@ -458,10 +501,10 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   a.nm_m = p.nm_m;
   a.dense_sink = p.dense_sink;
   a.dense_recent = p.dense_recent;
-  if (p.d == 128 && p.Br == 128) return launch<128, 128>(a, stream);
-  if (p.d == 128 && p.Br == 64) return launch<128, 64>(a, stream);
-  if (p.d == 64 && p.Br == 128) return launch<64, 128>(a, stream);
-  if (p.d == 64 && p.Br == 64) return launch<64, 64>(a, stream);
+  if (p.d == 128 && br_wg == 128) return launch<128, 128>(a, stream);
+  if (p.d == 128 && br_wg == 64) return launch<128, 64>(a, stream);
+  if (p.d == 64 && br_wg == 128) return launch<64, 128>(a, stream);
+  if (p.d == 64 && br_wg == 64) return launch<64, 64>(a, stream);
   return hipErrorInvalidValue;
 }
 

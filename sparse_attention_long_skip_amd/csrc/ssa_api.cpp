@@ -44,7 +44,8 @@ int check_prefill(const void* q, const void* k, const void* v, const void* out, 
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
     return SSA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return SSA_ERR_UNSUPPORTED;
-  if (Br != 64 && Br != 128) return SSA_ERR_UNSUPPORTED;
+  if (Br != 32 && Br != 64 && Br != 128) return SSA_ERR_UNSUPPORTED;
+  if (Br == 32 && block_idx) return SSA_ERR_UNSUPPORTED;
   if (Bc != kBc) return SSA_ERR_UNSUPPORTED;
   const long long nQ = ((long long)L + Br - 1) / Br;
   if ((long long)B * Hq * nQ >= (1ll << 31)) return SSA_ERR_UNSUPPORTED;

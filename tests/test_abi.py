@@ -70,7 +70,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, bi=FAKE) == -1          # block_idx without block_cnt
     assert _prefill(lib, bi=FAKE, bc=FAKE, mb=0) == -1
     assert _prefill(lib, d=96) == -2
-    assert _prefill(lib, Br=32) == -2
+    assert _prefill(lib, Br=16) == -2
+    assert _prefill(lib, Br=32, bi=FAKE, bc=FAKE, mb=4) == -2
     assert _prefill(lib, Bc=128) == -2
 
 

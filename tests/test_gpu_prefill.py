@@ -82,3 +82,16 @@ def test_deterministic_repeat():
     b = ssa.prefill(qd, kd, vd, -0.5, 128, 64, True, stats=True)
     torch.cuda.synchronize()
     assert torch.equal(a["out"], b["out"]) and torch.equal(a["tile_state"], b["tile_state"])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_wave_granular_votes(d):
+    # Br = 32: every 32-row wave decides alone (oracle with 32-row units)
+    q, k, v = _inputs(205, d, 2, 4, 2, 1000, d)
+    m = oracle.prefill(q, k, v, -math.inf, 32, 64, True, bits=True)["margin"]
+    for target in (0.3, 0.6):
+        lam = oracle.lambda_for_ratio(m, target)
+        r = prefill_parity(q, k, v, lam, 32, 64, True)
+        print(f"d={d} lam={lam:.3f}: skipped {r['skipped']}/{r['visited']} exempt {r['exempt']}")
+    r = prefill_parity(q, k, v, -math.inf, 32, 64, False)
+    assert r["skipped"] == 0
