@@ -247,6 +247,42 @@ def extra_sparse(args, torch, np, ssa, synth):
             "mfma_frac_executed": round(ex / (ev_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def extra_sparge(args, torch, np, ssa, synth):
+    """SpargeAttn two-stage filter on the 32K block-sparse shape with drifting
+    blocks: stage one (self-similarity gate, compressed map, Top-tau mass)
+    builds the lists, stage two (the skip rule) runs inside the prefill."""
+    c = synth.SPARGE
+    x = synth.prefill_inputs(c["cfg_id"], 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"],
+                             frac=c["frac"], drift=c["drift"])
+    q, k, v = (dev_bf16(x[n], torch, np) for n in ("q", "k", "v"))
+    del x
+    m = ssa.sparge_mask(q, k, c["theta"], c["tau"], "mass", c["pool"])
+    torch.cuda.synchronize()
+    cnt = m["block_cnt"]
+    nB = cnt.shape[-1]
+    n_causal = c["Hq"] * nB * (nB + 1) / 2
+    kw = dict(Br=64, Bc=64, causal=True, block_idx=m["block_idx"], block_cnt=cnt)
+    st = ssa.prefill(q, k, v, c["lam"], stats=True, **kw)
+    torch.cuda.synchronize()
+    state = st["tile_state"].cpu().numpy()
+    vis, kept = int((state != 0).sum()), int((state == 1).sum())
+    ws = m["workspace"]
+    fm = lambda: ssa.sparge_mask(q, k, c["theta"], c["tau"], "mass", c["pool"], workspace=ws)
+    ms_mask, ev_mask = time_launches(fm, 10, 3, torch)
+    out = torch.empty_like(q)
+    ms_p, ev_p = time_launches(lambda: ssa.prefill(q, k, v, c["lam"], out=out, **kw), 10, 3, torch)
+    ex = 2.0 * 64 * 64 * c["d"] * (vis + kept)
+    return {"workload": "SpargeAttn two-stage prefill 32K H=16 d=64, drifting blocks, "
+                        f"theta={c['theta']} tau={c['tau']} (P_hat mass), lambda={c['lam']}",
+            "mask_ms": round(ms_mask, 4),
+            "mask_hbm_gbs": round(2 * 2 * c["Hq"] * c["L"] * c["d"] / (ev_mask * 1e-3) / 1e9, 1),
+            "prefill_ms": round(ms_p, 4), "mask_density": round(vis / n_causal, 4),
+            "in_mask_skip_pct": round(100.0 * (vis - kept) / vis, 3),
+            "combined_sparsity": round(1 - kept / n_causal, 4),
+            "dense_equiv_tflops": round(dense_flops(c) / (ms_mask + ms_p) / 1e9, 1),
+            "mfma_frac_executed": round(ex / (ev_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def extra_nm(args, torch, np, ssa, synth):
     """N:M (2:4) sparse softmax on the 16K GQA shape, alone and with ~50% tile skipping."""
     from sparse_attention_long_skip_amd.calibrate import lambda_for_ratio
@@ -279,7 +315,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only-main", action="store_true", help="skip extra and cpu baseline (profiling)")
-    ap.add_argument("--leg", choices=["prefill_128k", "decode", "block_sparse_32k", "nm_2of4_16k"],
+    ap.add_argument("--leg", choices=["prefill_128k", "decode", "block_sparse_32k", "sparge_32k",
+                                      "nm_2of4_16k"],
                     help="run only this extra leg and print its JSON (profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the main leg, copy a 1 GiB buffer 5 times (HBM counter scale)")
@@ -298,7 +335,7 @@ def main():
     ssa.lib()
     torch.cuda.set_device(0)
     legs = {"prefill_128k": extra_128k, "decode": extra_decode, "block_sparse_32k": extra_sparse,
-            "nm_2of4_16k": extra_nm}
+            "sparge_32k": extra_sparge, "nm_2of4_16k": extra_nm}
     if args.leg:
         print(json.dumps({args.leg: legs[args.leg](args, torch, np, ssa, synth)}), flush=True)
         return

@@ -193,6 +193,60 @@ int ssa_block_mask(const void* q, const void* k, int B, int H, int L, int d, int
                    float* block_scores, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Top-tau selection modes of ssa_sparge_mask. */
+#define SSA_TAU_MASS 0
+#define SSA_TAU_COUNT 1
+
+/*
+ * ssa_sparge_mask_workspace_size -- bytes of device workspace ssa_sparge_mask
+ * needs (pooled Q and K, fp32 [B, H, nB, d] each, then the self-similarity
+ * of every Q and K block, fp32 [B, H, nB] each).
+ */
+size_t ssa_sparge_mask_workspace_size(int B, int H, int L, int d, int pool);
+
+/*
+ * ssa_sparge_mask -- SpargeAttn stage-one block mask (SpargeAttn page,
+ * two-stage online filter, stage one "sparse block online prediction":
+ * blocks whose tokens are similar are compressed to their mean token, a
+ * compressed attention map P_hat is built, and its Top-tau blocks are
+ * kept). Stage two is ssa_prefill's skip rule run over the returned lists.
+ *
+ *  q, k     [B, H, L, d] bf16, required (one KV head per query head).
+ *  Per block of pool tokens (the last may be short): self-similarity =
+ *  mean cosine similarity over all ordered token pairs of the block, self
+ *  pairs included (= squared norm of the mean unit row; a zero row counts
+ *  as a zero vector). A block is compressed iff its self-similarity > theta.
+ *  For a compressed query block b: P_hat[b, c] = softmax over the
+ *  compressed key blocks c <= b of q_bar[b] . k_bar[c] / sqrt(d) (fp32 block
+ *  means). Selection over those candidates, ranked by P_hat (ties: lower c
+ *  first):
+ *    tau_mode = SSA_TAU_MASS:  the smallest top set whose P_hat mass >= tau;
+ *    tau_mode = SSA_TAU_COUNT: the ceil(tau * n) best of the n candidates
+ *                              (the product and ceil in fp64).
+ *  Kept = the selection plus every uncompressed key block c <= b; an
+ *  uncompressed query block keeps every c <= b.
+ *  theta    any non-NaN float (> 1: nothing compressed, dense mask).
+ *  tau      in (0, 1].
+ *  block_idx [B, H, nB, max_blocks] int32, required: kept blocks ascending,
+ *           padded with -1; max_blocks >= nB = ceil(L / pool).
+ *  block_cnt [B, H, nB] int32, required.
+ *  block_sim [B, H, 2, nB] fp32, nullable: self-similarity of the Q blocks
+ *           (index 0) and K blocks (index 1).
+ *  block_scores [B, H, nB, nB] fp32, nullable: the pooled scores of every
+ *           causal pair (entries above the diagonal are -inf).
+ *  Only causal masks (causal = 1); d in {64, 128}; pool = 64; nB <= 4096.
+ *  The lists feed ssa_prefill with Br = Bc = pool.
+ *  workspace: at least ssa_sparge_mask_workspace_size(...) bytes, 16-byte
+ *           aligned; its contents on entry are ignored.
+ *  Errors: SSA_ERR_INVALID_ARG for missing pointers, bad sizes, theta NaN,
+ *  tau outside (0, 1], an unknown tau_mode or max_blocks < nB;
+ *  SSA_ERR_UNSUPPORTED for other d, pool or causal = 0.
+ */
+int ssa_sparge_mask(const void* q, const void* k, int B, int H, int L, int d, int pool,
+                    float theta, double tau, int tau_mode, int causal, int32_t* block_idx,
+                    int32_t* block_cnt, int max_blocks, float* block_sim, float* block_scores,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * ssa_lambda_from_scale_factor -- threshold from a context-length scale
  * factor (TRT-LLM page: the configured threshold_scale_factor is divided by

@@ -18,6 +18,9 @@ What it defines (sources: the pages on Skip-Softmax attention):
   sink block and local window (MInference page, block-sparse pattern and its
   ``block_sparse_attention(..., topk=64)`` call; NOSA page, section 3:
   ``init_blocks=1``, ``window_size=1024``, ``topk=64``).
+* ``block_mask.sparge_mask`` -- the SpargeAttn stage-one predictor: block
+  self-similarity gate, compressed attention map, top mass selection
+  (SpargeAttn page, stage one of the two-stage online filter).
 * ``calibrate.lambda_for_ratio`` -- the threshold that skips a target share
   of tiles, from the margins.
 * ``bruteforce`` -- a second, scalar-loop implementation for tiny inputs.
@@ -27,10 +30,11 @@ brute force and invariants.
 """
 
 from .attention import prefill, decode, replay, combine, visited_tiles, lse_combine_parts
-from .block_mask import pool_blocks, block_scores, block_mask
+from .block_mask import pool_blocks, block_scores, block_mask, block_self_similarity, sparge_mask
 from .calibrate import lambda_for_ratio, skip_ratio
 
 __all__ = [
     "prefill", "decode", "replay", "combine", "visited_tiles", "lse_combine_parts",
-    "pool_blocks", "block_scores", "block_mask", "lambda_for_ratio", "skip_ratio",
+    "pool_blocks", "block_scores", "block_mask", "block_self_similarity", "sparge_mask",
+    "lambda_for_ratio", "skip_ratio",
 ]

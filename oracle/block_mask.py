@@ -80,3 +80,92 @@ def block_mask(q, k, pool: int, topk: int, sink_blocks: int, window_tokens: int,
                 idx[b_, h, qb, :len(kept)] = kept
     return {"block_idx": idx, "block_cnt": cnt, "scores": scores, "kth": kth,
             "max_blocks": max_blocks}
+
+
+def block_self_similarity(x, pool: int, bits: bool = False) -> np.ndarray:
+    """Mean cosine similarity of the tokens of each block (SpargeAttn page,
+    stage one: blocks whose tokens are similar enough are compressed to one
+    mean token). Read as the mean over ALL ordered token pairs (i, j) of the
+    block, self pairs included: sim = || mean_i x_i / |x_i| ||^2. A zero row
+    counts as a zero vector."""
+    x = _widen(x, bits)
+    L = x.shape[-2]
+    nb = math.ceil(L / pool)
+    out = np.empty(x.shape[:-2] + (nb,))
+    for blk in range(nb):
+        xb = x[..., blk * pool:min(L, (blk + 1) * pool), :]
+        nrm = np.linalg.norm(xb, axis=-1, keepdims=True)
+        xh = np.where(nrm > 0, xb / np.where(nrm > 0, nrm, 1.0), 0.0)
+        mean = xh.mean(axis=-2)
+        out[..., blk] = (mean * mean).sum(axis=-1)
+    return out
+
+
+def sparge_mask(q, k, pool: int, theta: float, tau: float, tau_mode: str = "mass",
+                bits: bool = False) -> dict:
+    """SpargeAttn stage-one mask (SpargeAttn page, two-stage online filter,
+    stage one "sparse block online prediction"), causal. Readings:
+
+    * a query or key block is *compressed* when its self-similarity
+      (``block_self_similarity``) is above theta; it is then represented by
+      its mean token;
+    * the compressed map of query block b is P_hat[b, c] =
+      softmax over the compressed key blocks c <= b of
+      q_bar[b] . k_bar[c] / sqrt(d); uncompressed key blocks have no token,
+      take no part in the softmax and are always computed;
+    * Top-tau selection over the compressed candidates, ranked by P_hat
+      (ties: lower c first): ``tau_mode="mass"`` keeps the smallest top set
+      whose P_hat mass reaches tau; ``tau_mode="count"`` keeps the
+      ceil(tau * n) best of the n compressed candidates (ceil in fp64);
+    * an uncompressed query block keeps every causal block;
+    * lists are ascending.
+
+    Returns block_idx [B,H,nB,nB] (-1 padded), block_cnt, P_hat (0 outside
+    the compressed candidates), sim_q, sim_k and, per row, what decides the
+    cut for near-tie tests: ``mass_before`` / ``mass_at`` (the mass before and
+    after the last kept block, mass mode) and ``score_gap`` (score of the last
+    kept minus that of the first dropped candidate, inf when none drops)."""
+    if tau_mode not in ("mass", "count"):
+        raise ValueError(tau_mode)
+    scores = block_scores(q, k, pool, bits)
+    sim_q = block_self_similarity(q, pool, bits)
+    sim_k = block_self_similarity(k, pool, bits)
+    B, H, nb, _ = scores.shape
+    idx = np.full((B, H, nb, nb), -1, np.int64)
+    cnt = np.zeros((B, H, nb), np.int64)
+    phat = np.zeros_like(scores)
+    mass_before = np.full((B, H, nb), np.nan)
+    mass_at = np.full((B, H, nb), np.nan)
+    score_gap = np.full((B, H, nb), np.inf)
+    for b_ in range(B):
+        for h in range(H):
+            for qb in range(nb):
+                comp = [c for c in range(qb + 1) if sim_k[b_, h, c] > theta]
+                keep = set(c for c in range(qb + 1) if sim_k[b_, h, c] <= theta)
+                if sim_q[b_, h, qb] <= theta:
+                    keep = set(range(qb + 1))
+                elif comp:
+                    row = scores[b_, h, qb, comp]
+                    p = np.exp(row - row.max())
+                    p /= p.sum()
+                    phat[b_, h, qb, comp] = p
+                    order = sorted(range(len(comp)), key=lambda j: (-p[j], comp[j]))
+                    if tau_mode == "count":
+                        n_keep = math.ceil(tau * len(comp))
+                    else:
+                        acc, n_keep = 0.0, 0
+                        for j in order:
+                            if acc >= tau:
+                                break
+                            mass_before[b_, h, qb] = acc
+                            acc += p[j]
+                            n_keep += 1
+                        mass_at[b_, h, qb] = acc
+                    keep.update(comp[j] for j in order[:n_keep])
+                    if 0 < n_keep < len(comp):
+                        score_gap[b_, h, qb] = row[order[n_keep - 1]] - row[order[n_keep]]
+                kept = sorted(keep)
+                cnt[b_, h, qb] = len(kept)
+                idx[b_, h, qb, :len(kept)] = kept
+    return {"block_idx": idx, "block_cnt": cnt, "phat": phat, "sim_q": sim_q, "sim_k": sim_k,
+            "mass_before": mass_before, "mass_at": mass_at, "score_gap": score_gap}

@@ -155,3 +155,61 @@ def nm_attention(q, k, v, n, m, causal, dense_sink=0, dense_recent=0):
         out.append([sum(w[t] * float(v[c][e]) for t, c in enumerate(kept)) / tot for e in range(len(v[0]))])
         lses.append(mx + math.log(tot))
     return out, lses
+
+
+def sparge_blocks(q, k, pool, theta, tau, tau_mode="mass"):
+    """SpargeAttn stage-one mask for one head by explicit loops: pairwise
+    cosine similarities, explicit block means, a softmax over the compressed
+    key blocks, then a greedy pick of the most probable blocks."""
+    L, d = len(q), len(q[0])
+    nb = (L + pool - 1) // pool
+
+    def blk(x, b):
+        return x[b * pool:min(L, (b + 1) * pool)]
+
+    def sim(rows):
+        n = len(rows)
+        tot = 0.0
+        for a in rows:
+            for c in rows:
+                na = math.sqrt(sum(float(t) * float(t) for t in a))
+                nc = math.sqrt(sum(float(t) * float(t) for t in c))
+                if na > 0 and nc > 0:
+                    tot += _dot(a, c) / (na * nc)
+        return tot / (n * n)
+
+    def mean(rows):
+        return [sum(float(x[e]) for x in rows) / len(rows) for e in range(d)]
+
+    simk = [sim(blk(k, c)) for c in range(nb)]
+    res = []
+    for b in range(nb):
+        if sim(blk(q, b)) <= theta:
+            res.append(list(range(b + 1)))
+            continue
+        comp = [c for c in range(b + 1) if simk[c] > theta]
+        keep = [c for c in range(b + 1) if simk[c] <= theta]
+        if comp:
+            qb = mean(blk(q, b))
+            sc = {c: _dot(qb, mean(blk(k, c))) / math.sqrt(d) for c in comp}
+            mx = max(sc.values())
+            w = {c: math.exp(sc[c] - mx) for c in comp}
+            tot = sum(w.values())
+            left = list(comp)
+            picked, acc = [], 0.0
+            want = math.ceil(tau * len(comp)) if tau_mode == "count" else None
+            while left:
+                if want is not None and len(picked) == want:
+                    break
+                if want is None and acc >= tau:
+                    break
+                best = left[0]
+                for c in left:
+                    if w[c] > w[best]:
+                        best = c
+                left.remove(best)
+                picked.append(best)
+                acc += w[best] / tot
+            keep += picked
+        res.append(sorted(keep))
+    return res

@@ -1,8 +1,9 @@
 """Skip-Softmax sparse attention for AMD MI355X (gfx950).
 
 Causal GQA prefill with Skip-Softmax tile skipping, single-token split-K
-decode with a log-sum-exp combine, and a pooled-score top-k block mask for
-block-sparse prefill. The computation lives in hand-written HIP kernels
+decode with a log-sum-exp combine, N:M sparse softmax prefill, and two
+block-sparse prefill predictors (a pooled-score top-k mask and the SpargeAttn
+stage-one mask). The computation lives in hand-written HIP kernels
 behind the C ABI of ``include/ssa.h`` (``libssa.so``); this package is a thin
 ctypes binding that marshals torch tensors and the current stream.
 """
@@ -11,5 +12,6 @@ from ._lib import (  # noqa: F401
     SSAError, TILE_KEPT, TILE_SKIPPED, SSA_OK, SSA_ERR_INVALID_ARG, SSA_ERR_UNSUPPORTED,
     SSA_ERR_WORKSPACE, SSA_ERR_HIP, LIB_PATH, lib, status_string, abi_version,
     lambda_from_scale_factor, prefill, decode, decode_workspace_size, block_mask,
-    block_mask_max_blocks, block_mask_workspace_size,
+    block_mask_max_blocks, block_mask_workspace_size, sparge_mask, sparge_mask_workspace_size,
+    TAU_MODES,
 )

@@ -41,6 +41,9 @@ _SIGNATURES = {
     "ssa_block_mask_max_blocks": (_i, [_i, _i, _i, _i, _i]),
     "ssa_block_mask_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "ssa_block_mask": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _sz, _p]),
+    "ssa_sparge_mask_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "ssa_sparge_mask": (_i, [_p, _p, _i, _i, _i, _i, _i, _f, ctypes.c_double, _i, _i, _p, _p, _i, _p,
+                             _p, _p, _sz, _p]),
     "ssa_lambda_from_scale_factor": (_f, [_f, _i]),
     "ssa_status_string": (ctypes.c_char_p, [_i]),
     "ssa_abi_version": (_i, []),
@@ -228,4 +231,42 @@ def block_mask(q, k, pool: int = 64, topk: int = 64, sink_blocks: int = 1,
         _ptr(res["block_idx"]), _ptr(res["block_cnt"]), mb, _ptr(res["scores"]),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("ssa_block_mask", st)
+    return res
+
+
+TAU_MODES = {"mass": 0, "count": 1}
+
+
+def sparge_mask_workspace_size(B, H, L, d, pool=64) -> int:
+    return int(lib().ssa_sparge_mask_workspace_size(B, H, L, d, pool))
+
+
+def sparge_mask(q, k, theta: float, tau: float, tau_mode: str = "mass", pool: int = 64,
+                sim: bool = False, scores: bool = False, workspace=None, stream=None) -> dict:
+    """SpargeAttn stage-one mask (``ssa_sparge_mask``). q, k [B,H,L,d] bf16.
+    Returns block_idx [B,H,nB,nB] int32 (ascending, -1 padded), block_cnt
+    [B,H,nB] int32 and, if asked, the block self-similarities [B,H,2,nB]
+    and the pooled scores."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    if tau_mode not in TAU_MODES:
+        raise ValueError(f"tau_mode must be one of {sorted(TAU_MODES)}")
+    B, H, L, d = q.shape
+    nB = math.ceil(L / pool)
+    dev = q.device
+    need = sparge_mask_workspace_size(B, H, L, d, pool)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    res = {
+        "block_idx": torch.empty((B, H, nB, nB), dtype=torch.int32, device=dev),
+        "block_cnt": torch.empty((B, H, nB), dtype=torch.int32, device=dev),
+        "sim": torch.empty((B, H, 2, nB), dtype=torch.float32, device=dev) if sim else None,
+        "scores": torch.empty((B, H, nB, nB), dtype=torch.float32, device=dev) if scores else None,
+        "workspace": workspace,
+    }
+    st = lib().ssa_sparge_mask(
+        _ptr(q), _ptr(k), B, H, L, d, pool, float(theta), float(tau), TAU_MODES[tau_mode], 1,
+        _ptr(res["block_idx"]), _ptr(res["block_cnt"]), nB, _ptr(res["sim"]), _ptr(res["scores"]),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("ssa_sparge_mask", st)
     return res

@@ -52,10 +52,22 @@ struct MaskParams {
   void* workspace;
 };
 
+// SpargeAttn stage-one mask: m carries the shapes and outputs (topk, sink
+// and window unused); the workspace holds the pooled Q and K, then the
+// self-similarities of the Q and K blocks.
+struct SpargeParams {
+  MaskParams m;
+  float theta;
+  double tau;
+  int tau_mode;  // 0: P_hat mass, 1: count
+  float* block_sim;
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_block_mask(const MaskParams& p, hipStream_t stream);
+hipError_t launch_sparge_mask(const SpargeParams& p, hipStream_t stream);
 
 // Decode workspace layout: partial o [B, Hq, nS, d] fp32, then (m, l) [B, Hq, nS, 2] fp32.
 inline size_t decode_num_splits(int S_max, int Bc, int split_tiles) {
@@ -71,6 +83,11 @@ inline size_t decode_workspace_bytes(int B, int Hq, int S_max, int d, int Bc, in
 inline size_t mask_workspace_bytes(int B, int H, int L, int d, int pool) {
   size_t nB = ((size_t)L + pool - 1) / pool;
   return 2 * (size_t)B * H * nB * d * sizeof(float);
+}
+
+inline size_t sparge_workspace_bytes(int B, int H, int L, int d, int pool) {
+  size_t nB = ((size_t)L + pool - 1) / pool;
+  return mask_workspace_bytes(B, H, L, d, pool) + 2 * (size_t)B * H * nB * sizeof(float);
 }
 
 }  // namespace ssa

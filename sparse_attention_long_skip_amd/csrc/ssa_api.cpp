@@ -106,6 +106,28 @@ int check_mask(const void* q, const void* k, int B, int H, int L, int d, int poo
   return SSA_OK;
 }
 
+int check_sparge(const void* q, const void* k, int B, int H, int L, int d, int pool, float theta,
+                 double tau, int tau_mode, int causal, const int32_t* block_idx,
+                 const int32_t* block_cnt, int max_blocks, const void* ws, size_t ws_bytes) {
+  if (!q || !k || !block_idx || !block_cnt) return SSA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || L <= 0 || d <= 0 || pool <= 0) return SSA_ERR_INVALID_ARG;
+  if (isnan(theta) || !(tau > 0.0 && tau <= 1.0)) return SSA_ERR_INVALID_ARG;
+  if (tau_mode != SSA_TAU_MASS && tau_mode != SSA_TAU_COUNT) return SSA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return SSA_ERR_INVALID_ARG;
+  if (!sizes_ok({B, H, L, d})) return SSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(block_idx, 4) || !aligned(block_cnt, 4))
+    return SSA_ERR_INVALID_ARG;
+  const long long nB = ((long long)L + pool - 1) / pool;
+  if (max_blocks < nB) return SSA_ERR_INVALID_ARG;
+  if (!causal) return SSA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return SSA_ERR_UNSUPPORTED;
+  if (pool != 64) return SSA_ERR_UNSUPPORTED;
+  if (nB > kMaxMaskBlocks || (long long)B * H > 65535) return SSA_ERR_UNSUPPORTED;
+  if (!ws || !aligned(ws, 16)) return SSA_ERR_WORKSPACE;
+  if (ws_bytes < ssa::sparge_workspace_bytes(B, H, L, d, pool)) return SSA_ERR_WORKSPACE;
+  return SSA_OK;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? SSA_OK : SSA_ERR_HIP; }
 
 }  // namespace
@@ -250,6 +272,38 @@ int ssa_block_mask(const void* q, const void* k, int B, int H, int L, int d, int
   p.block_scores = block_scores;
   p.workspace = workspace;
   return hip_status(ssa::launch_block_mask(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t ssa_sparge_mask_workspace_size(int B, int H, int L, int d, int pool) {
+  if (B <= 0 || H <= 0 || L <= 0 || d <= 0 || pool <= 0) return 0;
+  return ssa::sparge_workspace_bytes(B, H, L, d, pool);
+}
+
+int ssa_sparge_mask(const void* q, const void* k, int B, int H, int L, int d, int pool,
+                    float theta, double tau, int tau_mode, int causal, int32_t* block_idx,
+                    int32_t* block_cnt, int max_blocks, float* block_sim, float* block_scores,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_sparge(q, k, B, H, L, d, pool, theta, tau, tau_mode, causal, block_idx,
+                              block_cnt, max_blocks, workspace, workspace_bytes);
+  if (st != SSA_OK) return st;
+  ssa::SpargeParams p = {};
+  p.m.q = q;
+  p.m.k = k;
+  p.m.B = B;
+  p.m.H = H;
+  p.m.L = L;
+  p.m.d = d;
+  p.m.pool = pool;
+  p.m.block_idx = block_idx;
+  p.m.block_cnt = block_cnt;
+  p.m.max_blocks = max_blocks;
+  p.m.block_scores = block_scores;
+  p.m.workspace = workspace;
+  p.theta = theta;
+  p.tau = tau;
+  p.tau_mode = tau_mode;
+  p.block_sim = block_sim;
+  return hip_status(ssa::launch_sparge_mask(p, static_cast<hipStream_t>(stream)));
 }
 
 float ssa_lambda_from_scale_factor(float scale_factor, int L) {

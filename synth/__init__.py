@@ -15,6 +15,12 @@ plus a sink key):
 * ``round(frac * nblocks)`` key blocks of ``block`` tokens are drawn without
   replacement; ``plant`` * u is added to every key row in them.
 * ``sink`` * u is added to key 0 (on top of any planting).
+* Optional block drift (``drift`` > 0, for the block-similarity predictor
+  of the SpargeAttn page, whose premise is that neighbouring tokens are
+  alike): every block of ``block`` rows of Q (per query head) and of K gets
+  one shared vector a_j * w_j added to all its rows, with w_j a standard
+  normal vector and a_j uniform in [0, drift], so blocks range from
+  unrelated tokens (a_j near 0) to nearly identical ones.
 * Every value is rounded to bfloat16 with round-to-nearest-even.
 
 Every piece is drawn from its own ``numpy.random.SeedSequence`` keyed by
@@ -35,6 +41,7 @@ CHUNK_ROWS = 4096
 # stream ids inside one (config, seed, batch, kv head) key
 _S_U, _S_PLANT, _S_Q, _S_K, _S_V, _S_DQ = 0, 1, 2, 3, 4, 5
 _S_LENS = 6
+_S_DRIFT = 7
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -82,15 +89,30 @@ def _normal_rows(key, rows, d) -> np.ndarray:
     return out
 
 
+def _add_drift(x, key, block, drift):
+    """Add a_j * w_j to every row of block j (see the module docstring)."""
+    if drift <= 0:
+        return
+    L, d = x.shape
+    nb = math.ceil(L / block)
+    rng = _rng(*key)
+    amp = rng.uniform(0.0, drift, nb).astype(np.float32)
+    w = rng.standard_normal((nb, d), dtype=np.float32)
+    for j in range(nb):
+        x[j * block:min(L, (j + 1) * block)] += amp[j] * w[j]
+
+
 def _prefill_piece(args):
-    cfg, seed, b, kvh, G, L, d, block, frac, plant, sink, what, g = args
+    cfg, seed, b, kvh, G, L, d, block, frac, plant, sink, drift, what, g = args
     u = _direction(cfg, seed, b, kvh, d)
     if what == "q":
         x = _normal_rows((cfg, seed, b, kvh, _S_Q, g), L, d)
         x += np.float32(plant) * u
+        _add_drift(x, (cfg, seed, b, kvh, _S_DRIFT, 1 + g), block, drift)
         return bf16_bits(x)
     if what == "k":
         x = _normal_rows((cfg, seed, b, kvh, _S_K), L, d)
+        _add_drift(x, (cfg, seed, b, kvh, _S_DRIFT, 0), block, drift)
         nb = math.ceil(L / block)
         for blk in _planted_blocks(cfg, seed, b, kvh, nb, frac):
             x[blk * block:min(L, (blk + 1) * block)] += np.float32(plant) * u
@@ -117,7 +139,7 @@ def _run(fn, tasks, workers):
 
 def prefill_inputs(cfg: int, seed: int, B: int, Hq: int, Hkv: int, L: int, d: int,
                    block: int = 64, frac: float = 0.1, plant: float = 4.0, sink: float = 8.0,
-                   workers: int | None = None) -> dict:
+                   drift: float = 0.0, workers: int | None = None) -> dict:
     """Q [B,Hq,L,d], K and V [B,Hkv,L,d] as bfloat16 bit patterns (uint16).
 
     Query head hq belongs to KV head hq // (Hq // Hkv)."""
@@ -127,9 +149,9 @@ def prefill_inputs(cfg: int, seed: int, B: int, Hq: int, Hkv: int, L: int, d: in
     for b in range(B):
         for kvh in range(Hkv):
             for g in range(G):
-                tasks.append((cfg, seed, b, kvh, G, L, d, block, frac, plant, sink, "q", g))
-            tasks.append((cfg, seed, b, kvh, G, L, d, block, frac, plant, sink, "k", 0))
-            tasks.append((cfg, seed, b, kvh, G, L, d, block, frac, plant, sink, "v", 0))
+                tasks.append((cfg, seed, b, kvh, G, L, d, block, frac, plant, sink, drift, "q", g))
+            tasks.append((cfg, seed, b, kvh, G, L, d, block, frac, plant, sink, drift, "k", 0))
+            tasks.append((cfg, seed, b, kvh, G, L, d, block, frac, plant, sink, drift, "v", 0))
     res = _run(_prefill_piece, tasks, workers)
     q = np.empty((B, Hq, L, d), np.uint16)
     k = np.empty((B, Hkv, L, d), np.uint16)
@@ -218,3 +240,8 @@ CONFIGS = {
     4: dict(kind="sparse", B=1, Hq=16, Hkv=16, L=32768, d=64, Br=64, Bc=64, causal=True,
             frac=0.10, pool=64, topk=64, sink_blocks=1, window_tokens=1024, lam=-6.0),
 }
+
+# SpargeAttn two-stage workload: the block-sparse shape above with drifting
+# blocks, stage one (theta, tau) then the skip rule (lam) over its lists.
+SPARGE = dict(kind="sparge", cfg_id=5, B=1, Hq=16, Hkv=16, L=32768, d=64, Br=64, Bc=64,
+              causal=True, frac=0.10, drift=2.0, pool=64, theta=0.2, tau=0.9, lam=-6.0)

@@ -214,3 +214,61 @@ def mask_parity(q_bits, k_bits, pool, topk, sink, window, heads=None, band=BAND)
                     assert abs(sc[qb, c] - r["kth"][0, 0, qb]) < band, (b, h, qb, c)
                     n_ties += 1
     return {"ties": n_ties, "gpu": g, "refs": refs}
+
+
+SIM_BAND = 1e-4    # self-similarity vs theta
+MASS_BAND = 1e-4   # P_hat mass at the cut vs tau
+
+
+def sparge_parity(q_bits, k_bits, theta, tau, mode="mass", pool=64, heads=None):
+    """HIP SpargeAttn stage-one mask vs the oracle on the listed (b, h) heads.
+
+    Self-similarities and scores must agree to fp32 accuracy. Kept lists
+    must match exactly except in rows where the oracle sits within a band of
+    a decision: a block self-similarity within SIM_BAND of theta (the row's
+    own query block, or any candidate key block), the P_hat mass before or
+    after the last kept block within MASS_BAND of tau, or a score gap at the
+    cut below BAND. Such rows are counted and must still differ by at most
+    the one or two blocks at the cut."""
+    import sparse_attention_long_skip_amd as ssa
+    q, k = dev_bf16(q_bits), dev_bf16(k_bits)
+    g = ssa.sparge_mask(q, k, theta, tau, mode, pool, sim=True, scores=True)
+    torch.cuda.synchronize()
+    B, H, L, d = q_bits.shape
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    gi, gc = to_np(g["block_idx"]), to_np(g["block_cnt"])
+    gsim, gs = to_np(g["sim"]), to_np(g["scores"])
+    n_near = 0
+    refs = {}
+    for (b, h) in heads:
+        r = oracle.sparge_mask(q_bits[b:b + 1, h:h + 1], k_bits[b:b + 1, h:h + 1], pool, theta, tau,
+                               mode, bits=True)
+        refs[(b, h)] = r
+        sq, sk = r["sim_q"][0, 0], r["sim_k"][0, 0]
+        assert np.max(np.abs(gsim[b, h, 0] - sq)) < 2e-5
+        assert np.max(np.abs(gsim[b, h, 1] - sk)) < 2e-5
+        sc = oracle.block_scores(q_bits[b:b + 1, h:h + 1], k_bits[b:b + 1, h:h + 1], pool,
+                                 bits=True)[0, 0]
+        fin = np.isfinite(sc)
+        assert np.array_equal(np.isfinite(gs[b, h]), fin)
+        assert np.max(np.abs(gs[b, h][fin] - sc[fin])) < 1e-4
+        nB = len(sq)
+        near_k = np.abs(sk - theta) < SIM_BAND
+        first_near_k = int(np.argmax(near_k)) if near_k.any() else nB
+        for qb in range(nB):
+            got = gi[b, h, qb, :gc[b, h, qb]].tolist()
+            assert all(x == -1 for x in gi[b, h, qb, gc[b, h, qb]:])
+            assert got == sorted(set(got)) and all(0 <= c <= qb for c in got)
+            want = r["block_idx"][0, 0, qb, :r["block_cnt"][0, 0, qb]].tolist()
+            if got == want:
+                continue
+            near = (abs(sq[qb] - theta) < SIM_BAND or qb >= first_near_k
+                    or abs(r["mass_before"][0, 0, qb] - tau) < MASS_BAND
+                    or abs(r["mass_at"][0, 0, qb] - tau) < MASS_BAND
+                    or r["score_gap"][0, 0, qb] < BAND)
+            assert near, (b, h, qb, sorted(set(got) ^ set(want)))
+            if abs(sq[qb] - theta) >= SIM_BAND and qb < first_near_k:
+                assert len(set(got) ^ set(want)) <= 2, (b, h, qb)
+            n_near += 1
+    return {"near": n_near, "gpu": g, "refs": refs}

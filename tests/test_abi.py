@@ -127,3 +127,31 @@ def test_prefill_nm_validation(lib):
     assert call(2, 8) == -2
     assert call(1, 3) == -2
     assert call(2, 4, d=96) == -2
+
+
+def _sparge(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, B=1, H=2, L=32768, d=64, pool=64, theta=0.3, tau=0.9, mode=0, causal=1,
+             bi=FAKE, bc=FAKE, mb=512, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.ssa_sparge_mask(a["q"], a["k"], a["B"], a["H"], a["L"], a["d"], a["pool"],
+                               ctypes.c_float(a["theta"]), ctypes.c_double(a["tau"]), a["mode"],
+                               a["causal"], a["bi"], a["bc"], a["mb"], None, None, a["ws"], a["wsb"],
+                               None)
+
+
+def test_sparge_validation(lib):
+    assert _sparge(lib, bc=None) == -1
+    assert _sparge(lib, theta=float("nan")) == -1
+    assert _sparge(lib, tau=0.0) == -1
+    assert _sparge(lib, tau=1.5) == -1
+    assert _sparge(lib, tau=float("nan")) == -1
+    assert _sparge(lib, mode=2) == -1
+    assert _sparge(lib, mb=511) == -1
+    assert _sparge(lib, causal=0) == -2
+    assert _sparge(lib, pool=32, mb=1024) == -2
+    assert _sparge(lib, d=32) == -2
+    assert _sparge(lib, L=64 * 5000, mb=5000) == -2
+    assert _sparge(lib, ws=None) == -3
+    need = lib.ssa_sparge_mask_workspace_size(1, 2, 32768, 64, 64)
+    assert need == 2 * 2 * 512 * 64 * 4 + 2 * 2 * 512 * 4
+    assert _sparge(lib, wsb=need - 1) == -3

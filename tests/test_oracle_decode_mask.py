@@ -191,3 +191,80 @@ def test_calibration_on_oracle_margins_reproduces_ratio():
     got = (res["decision"] == SKIPPED)[vis].mean()
     assert abs(got - oracle.skip_ratio(m, lam)) < 1e-12
     assert abs(got - 0.3) < 0.03
+
+
+def test_self_similarity_closed_forms():
+    # identical rows -> 1; mutually orthogonal rows -> 1/n (self pairs only)
+    x = np.zeros((1, 1, 8, 8))
+    x[0, 0, :4] = [1, 2, 0, 0, 0, 0, 0, 0]
+    for i in range(4):
+        x[0, 0, 4 + i, i] = 3.0
+    s = oracle.block_self_similarity(x, 4)
+    np.testing.assert_allclose(s[0, 0], [1.0, 0.25], atol=1e-15)
+
+
+def test_sparge_mask_matches_bruteforce():
+    for seed in range(30):
+        rng = np.random.default_rng(seed)
+        L = int(rng.integers(4, 40))
+        d = int(rng.integers(2, 5))
+        pool = int(rng.choice([2, 4]))
+        q = rng.standard_normal((1, 1, L, d)) + rng.uniform(0, 2) * np.ones(d)
+        k = rng.standard_normal((1, 1, L, d)) + rng.uniform(0, 2) * np.ones(d)
+        theta = float(rng.uniform(0.1, 0.9))
+        tau = float(rng.uniform(0.3, 0.99))
+        mode = ("mass", "count")[seed % 2]
+        res = oracle.sparge_mask(q, k, pool, theta, tau, mode)
+        ref = bruteforce.sparge_blocks(q[0, 0], k[0, 0], pool, theta, tau, mode)
+        for b, kept in enumerate(ref):
+            got = res["block_idx"][0, 0, b, :res["block_cnt"][0, 0, b]].tolist()
+            assert got == kept, (seed, b)
+
+
+def test_sparge_mask_limits():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 2, 64, 8)) + 2.0
+    k = rng.standard_normal((1, 2, 64, 8)) + 2.0
+    # theta above every similarity: nothing is compressed -> dense
+    d = oracle.sparge_mask(q, k, 8, 1.5, 0.5)
+    assert np.array_equal(d["block_cnt"][0, 0], np.arange(1, 9))
+    assert np.all(d["phat"] == 0)
+    # everything compressed, tau tiny: exactly the argmax block per row
+    for mode in ("mass", "count"):
+        t = oracle.sparge_mask(q, k, 8, -1.0, 1e-9, mode)
+        assert np.all(t["block_cnt"] == 1)
+        np.testing.assert_array_equal(t["block_idx"][..., 0], t["phat"].argmax(axis=-1))
+        np.testing.assert_allclose(t["phat"].sum(axis=-1), 1.0, rtol=1e-12)
+    # count mode with tau = 1 keeps every block
+    f = oracle.sparge_mask(q, k, 8, -1.0, 1.0, "count")
+    assert np.array_equal(f["block_cnt"][0, 1], np.arange(1, 9))
+    # mass mode: the kept mass reaches tau and the set is the smallest such
+    r = oracle.sparge_mask(q, k, 8, -1.0, 0.8)
+    for h in range(2):
+        for b in range(8):
+            kept = r["block_idx"][0, h, b, :r["block_cnt"][0, h, b]]
+            p = r["phat"][0, h, b]
+            assert p[kept].sum() >= 0.8 - 1e-12
+            assert r["mass_before"][0, h, b] < 0.8 <= r["mass_at"][0, h, b]
+            drop = np.setdiff1d(np.arange(b + 1), kept)
+            if len(drop):
+                assert p[kept].min() >= p[drop].max()
+
+
+def test_sparge_mask_uncompressed_key_blocks_always_kept():
+    # keys: block 1 is pure noise in alternating directions (similarity 0),
+    # blocks 0, 2, 3 are constant rows (similarity 1)
+    d, pool = 4, 4
+    k = np.zeros((1, 1, 16, d))
+    k[0, 0, 0:4] = [1, 0, 0, 0]
+    k[0, 0, 4:8] = [[1, 0, 0, 0], [-1, 0, 0, 0], [0, 1, 0, 0], [0, -1, 0, 0]]
+    k[0, 0, 8:12] = [0, 0, 1, 0]
+    k[0, 0, 12:16] = [0, 0, 0, 1]
+    q = np.tile(np.array([0, 0, 0, 5.0]), (1, 1, 16, 1))
+    r = oracle.sparge_mask(q, k, pool, 0.5, 1e-6)
+    np.testing.assert_allclose(r["sim_k"][0, 0], [1, 0, 1, 1], atol=1e-15)
+    # row 3: block 3 (aligned with q) is the top; block 1 is uncompressed
+    assert r["block_idx"][0, 0, 3, :r["block_cnt"][0, 0, 3]].tolist() == [1, 3]
+    assert r["phat"][0, 0, 3, 1] == 0
+    # row 1: compressed candidates {0}; block 1 always kept
+    assert r["block_idx"][0, 0, 1, :r["block_cnt"][0, 0, 1]].tolist() == [0, 1]
