@@ -193,6 +193,36 @@ int ssa_block_mask(const void* q, const void* k, int B, int H, int L, int d, int
                    float* block_scores, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/*
+ * ssa_block_mask_compressed_workspace_size -- bytes of device workspace
+ * ssa_block_mask_compressed needs (pooled Q, fp32 [B, H, nB, d], then the
+ * compressed keys, fp32 [B, H, ceil(L / stride), d]).
+ */
+size_t ssa_block_mask_compressed_workspace_size(int B, int H, int L, int d, int pool);
+
+/*
+ * ssa_block_mask_compressed -- ssa_block_mask with the keys compressed by
+ * overlapping means (NOSA page, section 1: the CompressK module averages
+ * kernel_size=32 keys every stride=16 tokens; section 3: attention over the
+ * compressed keys picks the blocks, with init_blocks=1, window_size=1024,
+ * topk=64 kept as in ssa_block_mask).
+ *
+ *  Compressed key m = mean of keys [m*stride, min(L, m*stride + kernel_size)),
+ *  for every m with m*stride < L (fp32). Key block c is represented by the
+ *  windows that start in it (m in [c*pool/stride, (c+1)*pool/stride)), and
+ *  score(b, c) = max over those m of q_bar[b] . k_tilde[m] / sqrt(d), c <= b.
+ *  Selection, outputs, limits and errors as ssa_block_mask; in addition
+ *  kernel_size or stride <= 0 is SSA_ERR_INVALID_ARG, and only
+ *  kernel_size = 32, stride = 16 are built (else SSA_ERR_UNSUPPORTED).
+ *  workspace: at least ssa_block_mask_compressed_workspace_size(...) bytes,
+ *           16-byte aligned.
+ */
+int ssa_block_mask_compressed(const void* q, const void* k, int B, int H, int L, int d, int pool,
+                              int kernel_size, int stride, int topk, int sink_blocks,
+                              int window_tokens, int causal, int32_t* block_idx, int32_t* block_cnt,
+                              int max_blocks, float* block_scores, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Top-tau selection modes of ssa_sparge_mask. */
 #define SSA_TAU_MASS 0
 #define SSA_TAU_COUNT 1

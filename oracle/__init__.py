@@ -18,6 +18,9 @@ What it defines (sources: the pages on Skip-Softmax attention):
   sink block and local window (MInference page, block-sparse pattern and its
   ``block_sparse_attention(..., topk=64)`` call; NOSA page, section 3:
   ``init_blocks=1``, ``window_size=1024``, ``topk=64``).
+* ``block_mask.block_scores_compressed`` -- block scores from overlapping
+  mean-compressed keys (NOSA page, section 1: kernel_size=32, stride=16),
+  fed to the same top-k / sink / window selection.
 * ``block_mask.sparge_mask`` -- the SpargeAttn stage-one predictor: block
   self-similarity gate, compressed attention map, top mass selection
   (SpargeAttn page, stage one of the two-stage online filter).
@@ -30,11 +33,13 @@ brute force and invariants.
 """
 
 from .attention import prefill, decode, replay, combine, visited_tiles, lse_combine_parts
-from .block_mask import pool_blocks, block_scores, block_mask, block_self_similarity, sparge_mask
+from .block_mask import (pool_blocks, block_scores, block_mask, block_self_similarity, sparge_mask,
+                         compress_keys, block_scores_compressed)
 from .calibrate import lambda_for_ratio, skip_ratio
 
 __all__ = [
     "prefill", "decode", "replay", "combine", "visited_tiles", "lse_combine_parts",
     "pool_blocks", "block_scores", "block_mask", "block_self_similarity", "sparge_mask",
+    "compress_keys", "block_scores_compressed",
     "lambda_for_ratio", "skip_ratio",
 ]

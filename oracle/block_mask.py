@@ -50,6 +50,45 @@ def block_scores(q, k, pool: int, bits: bool = False) -> np.ndarray:
     return s
 
 
+def compress_keys(k, kernel: int, stride: int, bits: bool = False) -> np.ndarray:
+    """Overlapping mean compression of the keys (NOSA page, section 1, the
+    CompressK module: a sliding window of kernel_size=32 tokens moved by
+    stride=16, each window averaged into one compressed key). Window m
+    averages keys [m*stride, min(L, m*stride + kernel)); windows start at
+    every multiple of stride below L (the last ones may be short)."""
+    k = _widen(k, bits)
+    L = k.shape[-2]
+    nw = math.ceil(L / stride)
+    out = np.empty(k.shape[:-2] + (nw, k.shape[-1]))
+    for m in range(nw):
+        out[..., m, :] = k[..., m * stride:min(L, m * stride + kernel), :].mean(axis=-2)
+    return out
+
+
+def block_scores_compressed(q, k, pool: int, kernel: int, stride: int,
+                            bits: bool = False) -> np.ndarray:
+    """Block scores from overlapping compressed keys (NOSA page, sections 1
+    and 3: attention over the compressed keys picks the candidate blocks).
+    Reading: key block c (pool tokens) is represented by the compressed
+    windows that start inside it, m in [c*pool/stride, (c+1)*pool/stride),
+    and its score against query block b is the best of them:
+    score[b, c] = max_m q_bar[b] . k_tilde[m] / sqrt(d), for c <= b (-inf
+    above the diagonal). With kernel = stride = pool this is block_scores."""
+    if pool % stride:
+        raise ValueError("stride must divide pool")
+    qb = pool_blocks(q, pool, bits)
+    kt = compress_keys(k, kernel, stride, bits)
+    d = qb.shape[-1]
+    s = (qb @ np.swapaxes(kt, -1, -2)) / math.sqrt(d)  # [..., nB, nW]
+    nb, nw = qb.shape[-2], kt.shape[-2]
+    per = pool // stride
+    out = np.full(qb.shape[:-2] + (nb, nb), -np.inf)
+    for c in range(nb):
+        out[..., c] = s[..., c * per:min(nw, (c + 1) * per)].max(axis=-1)
+    out[..., np.triu_indices(nb, 1)[0], np.triu_indices(nb, 1)[1]] = -np.inf
+    return out
+
+
 def block_mask(q, k, pool: int, topk: int, sink_blocks: int, window_tokens: int,
                bits: bool = False, scores=None) -> dict:
     """Kept key blocks per query block. q, k [B,H,L,d]. Returns block_idx

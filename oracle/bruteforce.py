@@ -111,8 +111,10 @@ def decode_skip_set(q_rows, k, n, lam, Bc, T):
     return skipped
 
 
-def topk_blocks(q, k, pool, topk, sink_blocks, window_tokens):
-    """Block mask for one head by explicit loops: q, k [L][d]."""
+def topk_blocks(q, k, pool, topk, sink_blocks, window_tokens, kernel=None, stride=None):
+    """Block mask for one head by explicit loops: q, k [L][d]. With kernel
+    and stride, a key block's score is the best score of the overlapping
+    compressed windows (kernel tokens, every stride tokens) starting in it."""
     L, d = len(q), len(q[0])
     nb = (L + pool - 1) // pool
 
@@ -120,11 +122,15 @@ def topk_blocks(q, k, pool, topk, sink_blocks, window_tokens):
         return [sum(float(x[e]) for x in rows) / len(rows) for e in range(d)]
 
     qb = [mean(q[b * pool:min(L, (b + 1) * pool)]) for b in range(nb)]
-    kb = [mean(k[b * pool:min(L, (b + 1) * pool)]) for b in range(nb)]
+    if kernel is None:
+        kw = [[mean(k[c * pool:min(L, (c + 1) * pool)])] for c in range(nb)]
+    else:
+        kw = [[mean(k[s:min(L, s + kernel)]) for s in range(c * pool, min(L, (c + 1) * pool), stride)]
+              for c in range(nb)]
     W = -(-window_tokens // pool) if window_tokens > 0 else 0
     res = []
     for b in range(nb):
-        scored = [(-_dot(qb[b], kb[c]) / math.sqrt(d), c) for c in range(b + 1)]
+        scored = [(-max(_dot(qb[b], w) for w in kw[c]) / math.sqrt(d), c) for c in range(b + 1)]
         scored.sort()
         keep = {c for _, c in scored[:topk]}
         keep |= {c for c in range(min(sink_blocks, b + 1))}

@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     SSAError, TILE_KEPT, TILE_SKIPPED, SSA_OK, SSA_ERR_INVALID_ARG, SSA_ERR_UNSUPPORTED,
     SSA_ERR_WORKSPACE, SSA_ERR_HIP, LIB_PATH, lib, status_string, abi_version,
     lambda_from_scale_factor, prefill, decode, decode_workspace_size, block_mask,
+    block_mask_compressed_workspace_size,
     block_mask_max_blocks, block_mask_workspace_size, sparge_mask, sparge_mask_workspace_size,
     TAU_MODES,
 )

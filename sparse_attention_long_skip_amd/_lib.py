@@ -41,6 +41,9 @@ _SIGNATURES = {
     "ssa_block_mask_max_blocks": (_i, [_i, _i, _i, _i, _i]),
     "ssa_block_mask_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "ssa_block_mask": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _sz, _p]),
+    "ssa_block_mask_compressed_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "ssa_block_mask_compressed": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i,
+                                       _p, _p, _sz, _p]),
     "ssa_sparge_mask_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "ssa_sparge_mask": (_i, [_p, _p, _i, _i, _i, _i, _i, _f, ctypes.c_double, _i, _i, _p, _p, _i, _p,
                              _p, _p, _sz, _p]),
@@ -205,10 +208,12 @@ def block_mask_workspace_size(B, H, L, d, pool=64) -> int:
 
 def block_mask(q, k, pool: int = 64, topk: int = 64, sink_blocks: int = 1,
                window_tokens: int = 1024, scores: bool = False, workspace=None,
-               stream=None) -> dict:
+               stream=None, compress=None) -> dict:
     """Pooled-score block mask (``ssa_block_mask``). q, k [B,H,L,d] bf16.
     Returns block_idx [B,H,nB,max_blocks] int32 (ascending, -1 padded),
-    block_cnt [B,H,nB] int32 and, if asked, the pooled scores."""
+    block_cnt [B,H,nB] int32 and, if asked, the pooled scores. With
+    ``compress=(kernel_size, stride)`` the key blocks are scored by
+    overlapping compressed keys (``ssa_block_mask_compressed``)."""
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
     B, H, L, d = q.shape
@@ -217,7 +222,10 @@ def block_mask(q, k, pool: int = 64, topk: int = 64, sink_blocks: int = 1,
     mb = block_mask_max_blocks(L, pool, topk, sink_blocks, window_tokens)
     if mb < 0:
         raise ValueError("invalid block-mask sizes")
-    need = block_mask_workspace_size(B, H, L, d, pool)
+    if compress is None:
+        need = block_mask_workspace_size(B, H, L, d, pool)
+    else:
+        need = block_mask_compressed_workspace_size(B, H, L, d, pool)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     res = {
@@ -226,12 +234,25 @@ def block_mask(q, k, pool: int = 64, topk: int = 64, sink_blocks: int = 1,
         "scores": torch.empty((B, H, nB, nB), dtype=torch.float32, device=dev) if scores else None,
         "workspace": workspace,
     }
-    st = lib().ssa_block_mask(
-        _ptr(q), _ptr(k), B, H, L, d, pool, topk, sink_blocks, window_tokens, 1,
-        _ptr(res["block_idx"]), _ptr(res["block_cnt"]), mb, _ptr(res["scores"]),
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
-    _check("ssa_block_mask", st)
+    wsb = workspace.numel() * workspace.element_size()
+    if compress is None:
+        st = lib().ssa_block_mask(
+            _ptr(q), _ptr(k), B, H, L, d, pool, topk, sink_blocks, window_tokens, 1,
+            _ptr(res["block_idx"]), _ptr(res["block_cnt"]), mb, _ptr(res["scores"]),
+            _ptr(workspace), wsb, _stream(stream))
+        _check("ssa_block_mask", st)
+    else:
+        kernel_size, stride = compress
+        st = lib().ssa_block_mask_compressed(
+            _ptr(q), _ptr(k), B, H, L, d, pool, kernel_size, stride, topk, sink_blocks,
+            window_tokens, 1, _ptr(res["block_idx"]), _ptr(res["block_cnt"]), mb,
+            _ptr(res["scores"]), _ptr(workspace), wsb, _stream(stream))
+        _check("ssa_block_mask_compressed", st)
     return res
+
+
+def block_mask_compressed_workspace_size(B, H, L, d, pool=64) -> int:
+    return int(lib().ssa_block_mask_compressed_workspace_size(B, H, L, d, pool))
 
 
 TAU_MODES = {"mass": 0, "count": 1}

@@ -50,6 +50,7 @@ struct MaskParams {
   int max_blocks;
   float* block_scores;
   void* workspace;
+  int compressed = 0;  // 1: key blocks scored by overlapping 32-token windows, stride 16
 };
 
 // SpargeAttn stage-one mask: m carries the shapes and outputs (topk, sink
@@ -83,6 +84,14 @@ inline size_t decode_workspace_bytes(int B, int Hq, int S_max, int d, int Bc, in
 inline size_t mask_workspace_bytes(int B, int H, int L, int d, int pool) {
   size_t nB = ((size_t)L + pool - 1) / pool;
   return 2 * (size_t)B * H * nB * d * sizeof(float);
+}
+
+// Compressed-key mask: pooled Q [B, H, nB, d], then the key windows
+// [B, H, ceil(L / 16), d], fp32.
+inline size_t compressed_mask_workspace_bytes(int B, int H, int L, int d, int pool) {
+  size_t nB = ((size_t)L + pool - 1) / pool;
+  size_t nW = ((size_t)L + 15) / 16;
+  return (size_t)B * H * (nB + nW) * d * sizeof(float);
 }
 
 inline size_t sparge_workspace_bytes(int B, int H, int L, int d, int pool) {

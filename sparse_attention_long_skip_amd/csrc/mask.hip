@@ -52,7 +52,16 @@ struct MaskArgs {
   float tau;    // Top-tau share (mass mode compares in fp32)
   double tau_d; // the same share, for ceil(tau * n) in fp64 (count mode)
   int tau_mode; // 0: P_hat mass, 1: count
+  int nW;       // compressed key windows (overlap mode): ceil(L / kStride)
+  int q_only;   // pool kernel: grid z = batch, queries only
 };
+
+// Overlapping key compression (NOSA page, section 1: CompressK with
+// kernel_size=32, stride=16): window m averages keys [16m, 16m + 32); a key
+// block of 64 tokens owns the 4 windows that start inside it.
+constexpr int kStride = 16;
+constexpr int kKernel = 32;
+constexpr int kWinPerBlock = 64 / kStride;
 
 template <int D, bool SIM>
 __global__ __launch_bounds__(256) void pool_kernel(MaskArgs a) {
@@ -62,8 +71,8 @@ __global__ __launch_bounds__(256) void pool_kernel(MaskArgs a) {
   __shared__ float red[4];
   const int blk = blockIdx.x;
   const int hh = blockIdx.y;
-  const int b = blockIdx.z >> 1;
-  const bool is_k = blockIdx.z & 1;
+  const int b = a.q_only ? blockIdx.z : (blockIdx.z >> 1);
+  const bool is_k = a.q_only ? false : (blockIdx.z & 1);
   const size_t hb = (size_t)b * a.H + hh;
   const uint16_t* src = (is_k ? a.k : a.q) + hb * a.L * D;
   float* dst = (is_k ? a.kbar : a.qbar) + (hb * a.nB + blk) * D;
@@ -127,6 +136,37 @@ __global__ __launch_bounds__(256) void pool_kernel(MaskArgs a) {
   }
 }
 
+// Compressed keys of one 64-token block: the rows [64 blk, 64 blk + 80) (cut
+// at L) are staged in LDS as bf16, then each thread sums one channel of one
+// window. One workgroup per (block, head, batch).
+template <int D>
+__global__ __launch_bounds__(256) void compress_k_kernel(MaskArgs a) {
+  constexpr int CPR = D / 8;
+  constexpr int ROWS = (kWinPerBlock - 1) * kStride + kKernel;  // 80
+  __shared__ __attribute__((aligned(16))) uint16_t rows[ROWS][D];
+  const int blk = blockIdx.x;
+  const size_t hb = (size_t)blockIdx.z * a.H + blockIdx.y;
+  const uint16_t* src = a.k + hb * a.L * D;
+  const int r0 = blk * 64;
+  const int nr = min(ROWS, a.L - r0);
+  const int t = threadIdx.x;
+  for (int x = t; x < nr * CPR; x += 256) {
+    const int r = x / CPR, cc = x % CPR;
+    store16(&rows[r][cc * 8], load16(src + (size_t)(r0 + r) * D + cc * 8));
+  }
+  __syncthreads();
+  const int ch = t % D;
+  for (int w = t / D; w < kWinPerBlock; w += 256 / D) {
+    const int m = blk * kWinPerBlock + w;
+    if (m >= a.nW) break;
+    const int lo = w * kStride;
+    const int hi = min(lo + kKernel, nr);
+    float acc = 0.f;
+    for (int r = lo; r < hi; ++r) acc += __uint_as_float((uint32_t)rows[r][ch] << 16);
+    a.kbar[(hb * a.nW + m) * D + ch] = acc / (float)(hi - lo);
+  }
+}
+
 __device__ __forceinline__ uint32_t order_bits(float x) {
   const uint32_t u = __float_as_uint(x);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -148,7 +188,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 // tie, a lower index). A candidate is in the top-k iff its key is at least
 // the topk-th largest key. The kept set is compacted in ascending order with
 // wave ballots.
-template <int D, int QPB, bool SPARGE>
+template <int D, int QPB, bool SPARGE, bool COMP>
 __global__ __launch_bounds__(256) void select_kernel(MaskArgs a) {
   constexpr int NT = 256;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -168,23 +208,32 @@ __global__ __launch_bounds__(256) void select_kernel(MaskArgs a) {
   for (int x = t; x < nq * D; x += NT) qv[x / D][x % D] = a.qbar[(hb * a.nB + qb0 + x / D) * D + x % D];
   __syncthreads();
 
-  // Scores: each pooled key row is read once for all QPB query blocks.
-  const float* kb = a.kbar + hb * a.nB * D;
+  // Scores: each pooled key row is read once for all QPB query blocks. With
+  // compressed keys a block's score is the best of its windows.
+  const float* kb = a.kbar + hb * (COMP ? (size_t)a.nW : (size_t)a.nB) * D;
   for (int c = t; c < N_max; c += NT) {
     float acc[QPB];
 #pragma unroll
-    for (int q = 0; q < QPB; ++q) acc[q] = 0.f;
-    const float* kr = kb + (size_t)c * D;
-#pragma unroll 4
-    for (int e = 0; e < D; e += 4) {
-      const f32x4 kx = *reinterpret_cast<const f32x4*>(kr + e);
+    for (int q = 0; q < QPB; ++q) acc[q] = -INFINITY;
+    const int nwin = COMP ? min(kWinPerBlock, a.nW - c * kWinPerBlock) : 1;
+    for (int w = 0; w < nwin; ++w) {
+      const float* kr = kb + (size_t)(COMP ? c * kWinPerBlock + w : c) * D;
+      float part[QPB];
 #pragma unroll
-      for (int q = 0; q < QPB; ++q) {
-        acc[q] = fmaf(qv[q][e], kx[0], acc[q]);
-        acc[q] = fmaf(qv[q][e + 1], kx[1], acc[q]);
-        acc[q] = fmaf(qv[q][e + 2], kx[2], acc[q]);
-        acc[q] = fmaf(qv[q][e + 3], kx[3], acc[q]);
+      for (int q = 0; q < QPB; ++q) part[q] = 0.f;
+#pragma unroll 4
+      for (int e = 0; e < D; e += 4) {
+        const f32x4 kx = *reinterpret_cast<const f32x4*>(kr + e);
+#pragma unroll
+        for (int q = 0; q < QPB; ++q) {
+          part[q] = fmaf(qv[q][e], kx[0], part[q]);
+          part[q] = fmaf(qv[q][e + 1], kx[1], part[q]);
+          part[q] = fmaf(qv[q][e + 2], kx[2], part[q]);
+          part[q] = fmaf(qv[q][e + 3], kx[3], part[q]);
+        }
       }
+#pragma unroll
+      for (int q = 0; q < QPB; ++q) acc[q] = fmaxf(acc[q], part[q]);
     }
 #pragma unroll
     for (int q = 0; q < QPB; ++q) {
@@ -344,18 +393,28 @@ __global__ __launch_bounds__(256) void select_kernel(MaskArgs a) {
   if (lane == 0) a.block_cnt[hb * a.nB + qb] = base;
 }
 
-template <int D, bool SPARGE>
+template <int D, bool SPARGE, bool COMP>
 hipError_t launch(const MaskArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((pool_kernel<D, SPARGE>), dim3(a.nB, a.H, a.B * 2), dim3(256), 0, stream, a);
+  if (COMP) {
+    // query blocks: plain means; keys: overlapping windows
+    MaskArgs aq = a;
+    aq.q_only = 1;
+    hipLaunchKernelGGL((pool_kernel<D, false>), dim3(a.nB, a.H, a.B), dim3(256), 0, stream, aq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((compress_k_kernel<D>), dim3(a.nB, a.H, a.B), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((pool_kernel<D, SPARGE>), dim3(a.nB, a.H, a.B * 2), dim3(256), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t per_row = sizeof(uint64_t) + (SPARGE ? sizeof(float) : 0);
   if (a.nB <= 1024) {
     constexpr int QPB = 4;
-    hipLaunchKernelGGL((select_kernel<D, QPB, SPARGE>), dim3((a.nB + QPB - 1) / QPB, a.H, a.B),
+    hipLaunchKernelGGL((select_kernel<D, QPB, SPARGE, COMP>), dim3((a.nB + QPB - 1) / QPB, a.H, a.B),
                        dim3(256), QPB * a.nBp * per_row, stream, a);
   } else {
-    hipLaunchKernelGGL((select_kernel<D, 1, SPARGE>), dim3(a.nB, a.H, a.B), dim3(256),
+    hipLaunchKernelGGL((select_kernel<D, 1, SPARGE, COMP>), dim3(a.nB, a.H, a.B), dim3(256),
                        a.nBp * per_row, stream, a);
   }
   return hipGetLastError();
@@ -388,8 +447,14 @@ hipError_t launch_block_mask(const MaskParams& p, hipStream_t stream) {
   a.topk = p.topk;
   a.sink = p.sink_blocks;
   a.W = p.window_tokens > 0 ? (p.window_tokens + p.pool - 1) / p.pool : 0;
-  if (p.d == 128) return launch<128, false>(a, stream);
-  if (p.d == 64) return launch<64, false>(a, stream);
+  a.nW = (p.L + kStride - 1) / kStride;
+  if (p.compressed) {
+    if (p.d == 128) return launch<128, false, true>(a, stream);
+    if (p.d == 64) return launch<64, false, true>(a, stream);
+  } else {
+    if (p.d == 128) return launch<128, false, false>(a, stream);
+    if (p.d == 64) return launch<64, false, false>(a, stream);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -403,8 +468,8 @@ hipError_t launch_sparge_mask(const SpargeParams& p, hipStream_t stream) {
   a.tau = (float)p.tau;
   a.tau_d = p.tau;
   a.tau_mode = p.tau_mode;
-  if (p.m.d == 128) return launch<128, true>(a, stream);
-  if (p.m.d == 64) return launch<64, true>(a, stream);
+  if (p.m.d == 128) return launch<128, true, false>(a, stream);
+  if (p.m.d == 64) return launch<64, true, false>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -87,7 +87,8 @@ int mask_max_blocks(int L, int pool, int topk, int sink, int window) {
 
 int check_mask(const void* q, const void* k, int B, int H, int L, int d, int pool, int topk,
                int sink, int window, int causal, const int32_t* block_idx,
-               const int32_t* block_cnt, int max_blocks, const void* ws, size_t ws_bytes) {
+               const int32_t* block_cnt, int max_blocks, const void* ws, size_t ws_bytes,
+               bool compressed = false) {
   if (!q || !k || !block_idx || !block_cnt) return SSA_ERR_INVALID_ARG;
   if (B <= 0 || H <= 0 || L <= 0 || d <= 0 || pool <= 0) return SSA_ERR_INVALID_ARG;
   if (topk < 0 || sink < 0 || window < 0) return SSA_ERR_INVALID_ARG;
@@ -102,7 +103,9 @@ int check_mask(const void* q, const void* k, int B, int H, int L, int d, int poo
   const long long nB = ((long long)L + pool - 1) / pool;
   if (nB > kMaxMaskBlocks || (long long)B * H > 65535) return SSA_ERR_UNSUPPORTED;
   if (!ws || !aligned(ws, 16)) return SSA_ERR_WORKSPACE;
-  if (ws_bytes < ssa::mask_workspace_bytes(B, H, L, d, pool)) return SSA_ERR_WORKSPACE;
+  const size_t need = compressed ? ssa::compressed_mask_workspace_bytes(B, H, L, d, pool)
+                                 : ssa::mask_workspace_bytes(B, H, L, d, pool);
+  if (ws_bytes < need) return SSA_ERR_WORKSPACE;
   return SSA_OK;
 }
 
@@ -304,6 +307,41 @@ int ssa_sparge_mask(const void* q, const void* k, int B, int H, int L, int d, in
   p.tau_mode = tau_mode;
   p.block_sim = block_sim;
   return hip_status(ssa::launch_sparge_mask(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t ssa_block_mask_compressed_workspace_size(int B, int H, int L, int d, int pool) {
+  if (B <= 0 || H <= 0 || L <= 0 || d <= 0 || pool <= 0) return 0;
+  return ssa::compressed_mask_workspace_bytes(B, H, L, d, pool);
+}
+
+int ssa_block_mask_compressed(const void* q, const void* k, int B, int H, int L, int d, int pool,
+                              int kernel_size, int stride, int topk, int sink_blocks,
+                              int window_tokens, int causal, int32_t* block_idx, int32_t* block_cnt,
+                              int max_blocks, float* block_scores, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (kernel_size <= 0 || stride <= 0) return SSA_ERR_INVALID_ARG;
+  const int st = check_mask(q, k, B, H, L, d, pool, topk, sink_blocks, window_tokens, causal,
+                            block_idx, block_cnt, max_blocks, workspace, workspace_bytes, true);
+  if (st != SSA_OK) return st;
+  if (kernel_size != 32 || stride != 16) return SSA_ERR_UNSUPPORTED;
+  ssa::MaskParams p;
+  p.q = q;
+  p.k = k;
+  p.B = B;
+  p.H = H;
+  p.L = L;
+  p.d = d;
+  p.pool = pool;
+  p.topk = topk;
+  p.sink_blocks = sink_blocks;
+  p.window_tokens = window_tokens;
+  p.block_idx = block_idx;
+  p.block_cnt = block_cnt;
+  p.max_blocks = max_blocks;
+  p.block_scores = block_scores;
+  p.workspace = workspace;
+  p.compressed = 1;
+  return hip_status(ssa::launch_block_mask(p, static_cast<hipStream_t>(stream)));
 }
 
 float ssa_lambda_from_scale_factor(float scale_factor, int L) {

@@ -179,13 +179,14 @@ def decode_parity(y, lam, T, units=None, Bc=64):
             "gpu": g, "ref": ref}
 
 
-def mask_parity(q_bits, k_bits, pool, topk, sink, window, heads=None, band=BAND):
+def mask_parity(q_bits, k_bits, pool, topk, sink, window, heads=None, band=BAND, compress=None):
     """HIP block mask vs the oracle on the listed (b, h) heads. Kept sets must
     match except candidates whose oracle score lies within ``band`` of the
-    topk-th score of that row (near-ties)."""
+    topk-th score of that row (near-ties). ``compress=(kernel, stride)``
+    scores key blocks by overlapping compressed keys."""
     import sparse_attention_long_skip_amd as ssa
     q, k = dev_bf16(q_bits), dev_bf16(k_bits)
-    g = ssa.block_mask(q, k, pool, topk, sink, window, scores=True)
+    g = ssa.block_mask(q, k, pool, topk, sink, window, scores=True, compress=compress)
     torch.cuda.synchronize()
     B, H, L, d = q_bits.shape
     if heads is None:
@@ -195,8 +196,10 @@ def mask_parity(q_bits, k_bits, pool, topk, sink, window, heads=None, band=BAND)
     n_ties = 0
     refs = {}
     for (b, h) in heads:
-        r = oracle.block_mask(q_bits[b:b + 1, h:h + 1], k_bits[b:b + 1, h:h + 1], pool, topk, sink,
-                              window, bits=True)
+        qh, kh = q_bits[b:b + 1, h:h + 1], k_bits[b:b + 1, h:h + 1]
+        sc_ref = None if compress is None else oracle.block_scores_compressed(qh, kh, pool, *compress,
+                                                                              bits=True)
+        r = oracle.block_mask(qh, kh, pool, topk, sink, window, bits=True, scores=sc_ref)
         refs[(b, h)] = r
         nB = r["block_cnt"].shape[-1]
         assert gi.shape[-1] == r["max_blocks"]

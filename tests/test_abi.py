@@ -155,3 +155,22 @@ def test_sparge_validation(lib):
     need = lib.ssa_sparge_mask_workspace_size(1, 2, 32768, 64, 64)
     assert need == 2 * 2 * 512 * 64 * 4 + 2 * 2 * 512 * 4
     assert _sparge(lib, wsb=need - 1) == -3
+
+
+def test_compressed_mask_validation(lib):
+    def call(kernel=32, stride=16, **kw):
+        a = dict(q=FAKE, k=FAKE, B=1, H=2, L=32768, d=64, pool=64, topk=64, sink=1, win=1024,
+                 causal=1, bi=FAKE, bc=FAKE, mb=81, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.ssa_block_mask_compressed(a["q"], a["k"], a["B"], a["H"], a["L"], a["d"], a["pool"],
+                                             kernel, stride, a["topk"], a["sink"], a["win"], a["causal"],
+                                             a["bi"], a["bc"], a["mb"], None, a["ws"], a["wsb"], None)
+    assert call(kernel=0) == -1
+    assert call(stride=-1) == -1
+    assert call(bi=None) == -1
+    assert call(mb=80) == -1
+    assert call(kernel=64, stride=32) == -2
+    assert call(causal=0) == -2
+    need = lib.ssa_block_mask_compressed_workspace_size(1, 2, 32768, 64, 64)
+    assert need == 2 * (512 + 2048) * 64 * 4
+    assert call(wsb=need - 1) == -3

@@ -48,3 +48,19 @@ def test_mask_ties_prefer_lower_index():
     idx, cnt = g["block_idx"].cpu().numpy(), g["block_cnt"].cpu().numpy()
     for b in range(40):
         assert idx[0, 0, b, :cnt[0, 0, b]].tolist() == list(range(min(5, b + 1)))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("L,topk,sink,win", [(1000, 4, 1, 128), (4096, 16, 2, 256), (333, 64, 1, 1024),
+                                             (64 * 70 + 40, 8, 1, 64)])
+def test_compressed_mask(d, L, topk, sink, win):
+    # NOSA overlapping key compression: windows of 32 keys every 16
+    x = synth.prefill_inputs(403, L, 1, 3, 3, L, d)
+    r = mask_parity(x["q"], x["k"], 64, topk, sink, win, compress=(32, 16))
+    print(f"d={d} L={L}: near-tie differences {r['ties']}")
+
+
+def test_compressed_mask_long_sequence():
+    x = synth.prefill_inputs(404, 0, 1, 1, 1, 1100 * 64 - 17, 64)
+    r = mask_parity(x["q"], x["k"], 64, 64, 1, 1024, compress=(32, 16))
+    print(f"near-tie differences {r['ties']}")

@@ -268,3 +268,50 @@ def test_sparge_mask_uncompressed_key_blocks_always_kept():
     assert r["phat"][0, 0, 3, 1] == 0
     # row 1: compressed candidates {0}; block 1 always kept
     assert r["block_idx"][0, 0, 1, :r["block_cnt"][0, 0, 1]].tolist() == [0, 1]
+
+
+def test_compressed_keys_closed_forms():
+    # keys 0..L-1 along one axis: window m averages m*stride .. m*stride+kernel-1
+    L = 50
+    k = np.arange(L, dtype=np.float64).reshape(1, 1, L, 1)
+    kt = oracle.compress_keys(k, 32, 16)
+    assert kt.shape[-2] == 4
+    np.testing.assert_allclose(kt[0, 0, :, 0], [15.5, 31.5, (32 + 49) / 2, (48 + 49) / 2])
+    # kernel = stride = pool reduces to the plain pooled scores
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((2, 3, 300, 8))
+    kk = rng.standard_normal((2, 3, 300, 8))
+    np.testing.assert_allclose(oracle.block_scores_compressed(q, kk, 64, 64, 64),
+                               oracle.block_scores(q, kk, 64), rtol=1e-12, atol=1e-12)
+
+
+def test_compressed_block_mask_matches_bruteforce():
+    for seed in range(12):
+        rng = np.random.default_rng(100 + seed)
+        L = int(rng.integers(10, 90))
+        d = int(rng.integers(2, 5))
+        pool, kernel, stride = [(8, 8, 4), (8, 4, 2), (4, 4, 2), (8, 16, 4)][seed % 4]
+        topk, sink, win = int(rng.integers(0, 5)), int(rng.integers(0, 2)), int(rng.integers(0, 20))
+        q = rng.standard_normal((1, 1, L, d))
+        k = rng.standard_normal((1, 1, L, d))
+        sc = oracle.block_scores_compressed(q, k, pool, kernel, stride)
+        got = oracle.block_mask(q, k, pool, topk, sink, win, scores=sc)
+        ref = bruteforce.topk_blocks(q[0, 0], k[0, 0], pool, topk, sink, win, kernel, stride)
+        for b, kept in enumerate(ref):
+            assert got["block_idx"][0, 0, b, :got["block_cnt"][0, 0, b]].tolist() == kept, (seed, b)
+
+
+def test_compressed_scores_see_a_spike_the_block_mean_dilutes():
+    # one key block holds a short run of keys aligned with the query: the
+    # 32-token windows see it at full strength, the 64-token mean at half
+    d, L = 4, 256
+    q = np.zeros((1, 1, L, d))
+    q[..., 0] = 1.0
+    k = np.zeros((1, 1, L, d))
+    k[0, 0, 64 + 16:64 + 48, 0] = 2.0   # 32 keys in block 1, exactly window m = 5
+    k[0, 0, 128:192, 0] = 1.2           # block 2: a weaker but uniform run
+    plain = oracle.block_scores(q, k, 64)
+    comp = oracle.block_scores_compressed(q, k, 64, 32, 16)
+    assert plain[0, 0, 3, 1] < plain[0, 0, 3, 2]
+    assert comp[0, 0, 3, 1] > comp[0, 0, 3, 2]
+    np.testing.assert_allclose(comp[0, 0, 3, 1], 2.0 / 2.0, rtol=1e-12)   # 2.0 / sqrt(4)
