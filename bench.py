@@ -283,6 +283,42 @@ def extra_sparge(args, torch, np, ssa, synth):
             "mfma_frac_executed": round(ex / (ev_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def extra_vslash(args, torch, np, ssa, synth):
+    """Vertical-slash estimator (last 64 queries, 1000 vertical keys, 64
+    slash offsets) and the block-sparse prefill over its tile cover, on the
+    32K block-sparse shape."""
+    c = synth.CONFIGS[4]
+    x = synth.prefill_inputs(4, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"], frac=c["frac"])
+    q, k, v = (dev_bf16(x[n], torch, np) for n in ("q", "k", "v"))
+    del x
+    nv, ns, R = 1000, 64, 64
+    m = ssa.vertical_slash_mask(q, k, nv, ns, R)
+    torch.cuda.synchronize()
+    cnt = m["block_cnt"]
+    nB = cnt.shape[-1]
+    n_causal = c["Hq"] * nB * (nB + 1) / 2
+    kw = dict(Br=64, Bc=64, causal=True, block_idx=m["block_idx"], block_cnt=cnt)
+    st = ssa.prefill(q, k, v, c["lam"], stats=True, **kw)
+    torch.cuda.synchronize()
+    state = st["tile_state"].cpu().numpy()
+    vis, kept = int((state != 0).sum()), int((state == 1).sum())
+    ws = m["workspace"]
+    ms_mask, ev_mask = time_launches(lambda: ssa.vertical_slash_mask(q, k, nv, ns, R, workspace=ws),
+                                     10, 3, torch)
+    out = torch.empty_like(q)
+    ms_p, ev_p = time_launches(lambda: ssa.prefill(q, k, v, c["lam"], out=out, **kw), 10, 3, torch)
+    ex = 2.0 * 64 * 64 * c["d"] * (vis + kept)
+    return {"workload": f"vertical-slash estimator 32K H=16 d=64 (last {R} queries, {nv} vertical, "
+                        f"{ns} slash) + block-sparse prefill over its tiles, lambda={c['lam']}",
+            "estimator_ms": round(ms_mask, 4),
+            "estimator_k_read_gbs": round(c["Hq"] * c["L"] * c["d"] * 2 / (ev_mask * 1e-3) / 1e9, 1),
+            "prefill_ms": round(ms_p, 4), "mask_density": round(vis / n_causal, 4),
+            "in_mask_skip_pct": round(100.0 * (vis - kept) / vis, 3),
+            "combined_sparsity": round(1 - kept / n_causal, 4),
+            "dense_equiv_tflops": round(dense_flops(c) / (ms_mask + ms_p) / 1e9, 1),
+            "mfma_frac_executed": round(ex / (ev_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def extra_nm(args, torch, np, ssa, synth):
     """N:M (2:4) sparse softmax on the 16K GQA shape, alone and with ~50% tile skipping."""
     from sparse_attention_long_skip_amd.calibrate import lambda_for_ratio
@@ -316,7 +352,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only-main", action="store_true", help="skip extra and cpu baseline (profiling)")
     ap.add_argument("--leg", choices=["prefill_128k", "decode", "block_sparse_32k", "sparge_32k",
-                                      "nm_2of4_16k"],
+                                      "vslash_32k", "nm_2of4_16k"],
                     help="run only this extra leg and print its JSON (profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the main leg, copy a 1 GiB buffer 5 times (HBM counter scale)")
@@ -335,7 +371,7 @@ def main():
     ssa.lib()
     torch.cuda.set_device(0)
     legs = {"prefill_128k": extra_128k, "decode": extra_decode, "block_sparse_32k": extra_sparse,
-            "sparge_32k": extra_sparge, "nm_2of4_16k": extra_nm}
+            "sparge_32k": extra_sparge, "vslash_32k": extra_vslash, "nm_2of4_16k": extra_nm}
     if args.leg:
         print(json.dumps({args.leg: legs[args.leg](args, torch, np, ssa, synth)}), flush=True)
         return

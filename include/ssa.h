@@ -278,6 +278,50 @@ int ssa_sparge_mask(const void* q, const void* k, int B, int H, int L, int d, in
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ssa_vertical_slash_workspace_size -- bytes of device workspace
+ * ssa_vertical_slash_mask needs (row statistics, column and diagonal scores
+ * and their partials, tile flags and prefix counts).
+ */
+size_t ssa_vertical_slash_workspace_size(int B, int H, int L);
+
+/*
+ * ssa_vertical_slash_mask -- vertical-slash block estimator (MInference
+ * page: the vertical-slash pattern is estimated by attending from the last
+ * query vector(s) to every key, which picks the best vertical lines and
+ * slash lines; its vertical_slash_sparse_attention(vertical_topk, slash)).
+ *
+ *  q, k     [B, H, L, d] bf16, required (one KV head per query head).
+ *  The last last_q query rows i (positions p_i = L - last_q + i) attend
+ *  causally: A[i, j] = softmax over j <= p_i of q_i . k_j / sqrt(d), fp32.
+ *  Vertical score v[j] = sum_i A[i, j]; slash score s[o] = sum_i A[i, p_i - o]
+ *  (o = 0 is the main diagonal). The n_vertical keys and n_slash offsets
+ *  with the highest scores are chosen (ties: lower index first; a count of
+ *  L or more takes all).
+ *  Tiles of pool x pool: tile (b, c), c <= b, is listed iff it holds an
+ *  entry (r, j), j <= r, with j a chosen vertical or r - j a chosen slash.
+ *  The prefill then computes every listed tile in full (a superset of the
+ *  line pattern at tile granularity).
+ *  block_idx [B, H, nB, max_blocks] int32, required: ascending, -1 padded;
+ *           max_blocks >= nB = ceil(L / pool).
+ *  block_cnt [B, H, nB] int32, required.
+ *  vertical_idx [B, H, n_vertical] int32, nullable: chosen keys, ascending
+ *           (-1 padded when n_vertical > L). slash_idx likewise for offsets.
+ *  vertical_scores, slash_scores [B, H, L] fp32, nullable: v and s.
+ *  1 <= last_q <= min(L, 64); n_vertical, n_slash >= 0; causal = 1;
+ *  d in {64, 128}; pool = 64; nB <= 4096.
+ *  workspace: at least ssa_vertical_slash_workspace_size(B, H, L) bytes,
+ *           256-byte aligned; contents on entry are ignored.
+ *  Errors: SSA_ERR_INVALID_ARG for missing pointers, bad sizes, last_q
+ *  outside [1, L], negative counts or max_blocks < nB; SSA_ERR_UNSUPPORTED
+ *  for causal = 0, other d or pool, or last_q > 64.
+ */
+int ssa_vertical_slash_mask(const void* q, const void* k, int B, int H, int L, int d, int last_q,
+                            int n_vertical, int n_slash, int pool, int causal, int32_t* block_idx,
+                            int32_t* block_cnt, int max_blocks, int32_t* vertical_idx,
+                            int32_t* slash_idx, float* vertical_scores, float* slash_scores,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * ssa_lambda_from_scale_factor -- threshold from a context-length scale
  * factor (TRT-LLM page: the configured threshold_scale_factor is divided by
  * the context length to give the actual threshold, so longer contexts skip

@@ -24,6 +24,9 @@ What it defines (sources: the pages on Skip-Softmax attention):
 * ``block_mask.sparge_mask`` -- the SpargeAttn stage-one predictor: block
   self-similarity gate, compressed attention map, top mass selection
   (SpargeAttn page, stage one of the two-stage online filter).
+* ``vertical_slash.vertical_slash_mask`` -- the vertical-slash estimator
+  (MInference page: the last query rows score every key; the best columns
+  and diagonals are kept) and the tiles that cover them.
 * ``calibrate.lambda_for_ratio`` -- the threshold that skips a target share
   of tiles, from the margins.
 * ``bruteforce`` -- a second, scalar-loop implementation for tiny inputs.
@@ -36,10 +39,12 @@ from .attention import prefill, decode, replay, combine, visited_tiles, lse_comb
 from .block_mask import (pool_blocks, block_scores, block_mask, block_self_similarity, sparge_mask,
                          compress_keys, block_scores_compressed)
 from .calibrate import lambda_for_ratio, skip_ratio
+from .vertical_slash import vertical_slash_scores, vertical_slash_mask, cover_blocks
 
 __all__ = [
     "prefill", "decode", "replay", "combine", "visited_tiles", "lse_combine_parts",
     "pool_blocks", "block_scores", "block_mask", "block_self_similarity", "sparge_mask",
     "compress_keys", "block_scores_compressed",
     "lambda_for_ratio", "skip_ratio",
+    "vertical_slash_scores", "vertical_slash_mask", "cover_blocks",
 ]

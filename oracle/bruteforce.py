@@ -219,3 +219,40 @@ def sparge_blocks(q, k, pool, theta, tau, tau_mode="mass"):
             keep += picked
         res.append(sorted(keep))
     return res
+
+
+def vertical_slash(q, k, last_q, n_vertical, n_slash, pool):
+    """Vertical-slash estimate and tile cover for one head by explicit loops:
+    the attention rows of the last queries, column and diagonal sums, greedy
+    picks, then every allowed entry (r, j) on a chosen line marks its tile."""
+    L, d = len(q), len(q[0])
+    v = [0.0] * L
+    s = [0.0] * L
+    for p in range(L - last_q, L):
+        sc = [_dot(q[p], k[j]) / math.sqrt(d) for j in range(p + 1)]
+        mx = max(sc)
+        w = [math.exp(x - mx) for x in sc]
+        tot = sum(w)
+        for j in range(p + 1):
+            v[j] += w[j] / tot
+            s[p - j] += w[j] / tot
+
+    def pick(x, n):
+        left, out = list(range(L)), []
+        while left and len(out) < n:
+            best = left[0]
+            for i in left:
+                if x[i] > x[best]:
+                    best = i
+            left.remove(best)
+            out.append(best)
+        return set(out)
+
+    vs, ss = pick(v, n_vertical), pick(s, n_slash)
+    nb = (L + pool - 1) // pool
+    tiles = [set() for _ in range(nb)]
+    for r in range(L):
+        for j in range(r + 1):
+            if j in vs or (r - j) in ss:
+                tiles[r // pool].add(j // pool)
+    return [sorted(t) for t in tiles], sorted(vs), sorted(ss), v, s

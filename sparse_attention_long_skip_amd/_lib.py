@@ -47,6 +47,9 @@ _SIGNATURES = {
     "ssa_sparge_mask_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "ssa_sparge_mask": (_i, [_p, _p, _i, _i, _i, _i, _i, _f, ctypes.c_double, _i, _i, _p, _p, _i, _p,
                              _p, _p, _sz, _p]),
+    "ssa_vertical_slash_workspace_size": (_sz, [_i, _i, _i]),
+    "ssa_vertical_slash_mask": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p,
+                                     _p, _p, _p, _sz, _p]),
     "ssa_lambda_from_scale_factor": (_f, [_f, _i]),
     "ssa_status_string": (ctypes.c_char_p, [_i]),
     "ssa_abi_version": (_i, []),
@@ -290,4 +293,45 @@ def sparge_mask(q, k, theta: float, tau: float, tau_mode: str = "mass", pool: in
         _ptr(res["block_idx"]), _ptr(res["block_cnt"]), nB, _ptr(res["sim"]), _ptr(res["scores"]),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("ssa_sparge_mask", st)
+    return res
+
+
+def vertical_slash_workspace_size(B, H, L) -> int:
+    return int(lib().ssa_vertical_slash_workspace_size(B, H, L))
+
+
+def vertical_slash_mask(q, k, n_vertical: int, n_slash: int, last_q: int = 64, pool: int = 64,
+                        indices: bool = False, scores: bool = False, workspace=None,
+                        stream=None) -> dict:
+    """Vertical-slash block estimator (``ssa_vertical_slash_mask``). q, k
+    [B,H,L,d] bf16. Returns block_idx [B,H,nB,nB] int32 (ascending, -1
+    padded), block_cnt [B,H,nB] int32 and, if asked, the chosen vertical keys
+    and slash offsets (``indices``) and the scores v, s (``scores``)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k, "k", torch.bfloat16, 4)
+    B, H, L, d = q.shape
+    nB = math.ceil(L / pool)
+    dev = q.device
+    need = vertical_slash_workspace_size(B, H, L)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    res = {
+        "block_idx": torch.empty((B, H, nB, nB), **i32),
+        "block_cnt": torch.empty((B, H, nB), **i32),
+        "vertical": torch.empty((B, H, max(n_vertical, 1)), **i32) if indices else None,
+        "slash": torch.empty((B, H, max(n_slash, 1)), **i32) if indices else None,
+        "v": torch.empty((B, H, L), **f32) if scores else None,
+        "s": torch.empty((B, H, L), **f32) if scores else None,
+        "workspace": workspace,
+    }
+    st = lib().ssa_vertical_slash_mask(
+        _ptr(q), _ptr(k), B, H, L, d, last_q, n_vertical, n_slash, pool, 1,
+        _ptr(res["block_idx"]), _ptr(res["block_cnt"]), nB,
+        _ptr(res["vertical"]) if n_vertical > 0 else None,
+        _ptr(res["slash"]) if n_slash > 0 else None,
+        _ptr(res["v"]), _ptr(res["s"]), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("ssa_vertical_slash_mask", st)
     return res

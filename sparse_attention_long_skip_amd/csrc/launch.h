@@ -64,11 +64,56 @@ struct SpargeParams {
   float* block_sim;
 };
 
+// Vertical-slash estimator: scores of the last last_q (<= 64) query rows,
+// top vertical keys and slash offsets, and the 64 x 64 tiles covering them.
+struct VsParams {
+  const void* q;
+  const void* k;
+  int B, H, L, d, last_q, n_vertical, n_slash;
+  int32_t* block_idx;
+  int32_t* block_cnt;
+  int max_blocks;
+  int32_t* vertical_idx;
+  int32_t* slash_idx;
+  float* vertical_scores;
+  float* slash_scores;
+  void* workspace;
+};
+
+constexpr int kVsChunk = 256;           // keys per workgroup in the scoring passes
+constexpr int kVsSpw = kVsChunk + 64;   // per-chunk diagonal partials (chunk + last_q - 1)
+
+// Workspace of the vertical-slash estimator: byte offsets of each array,
+// every one 256-byte aligned.
+struct VsWorkspace {
+  size_t part, stats, v, s, spart, vt, P, total;
+  VsWorkspace(int B, int H, int L) {
+    const size_t BH = (size_t)B * H;
+    const size_t nchunk = ((size_t)L + kVsChunk - 1) / kVsChunk;
+    const size_t nB = ((size_t)L + 63) / 64;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+      const size_t o = off;
+      off += (bytes + 255) & ~(size_t)255;
+      return o;
+    };
+    part = take(BH * nchunk * 64 * 2 * sizeof(float));
+    stats = take(BH * 64 * 2 * sizeof(float));
+    v = take(BH * L * sizeof(float));
+    s = take(BH * L * sizeof(float));
+    spart = take(BH * nchunk * kVsSpw * sizeof(float));
+    vt = take(BH * nB * sizeof(int32_t));
+    P = take(BH * ((size_t)L + 1) * sizeof(int32_t));
+    total = off;
+  }
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_block_mask(const MaskParams& p, hipStream_t stream);
 hipError_t launch_sparge_mask(const SpargeParams& p, hipStream_t stream);
+hipError_t launch_vertical_slash(const VsParams& p, hipStream_t stream);
 
 // Decode workspace layout: partial o [B, Hq, nS, d] fp32, then (m, l) [B, Hq, nS, 2] fp32.
 inline size_t decode_num_splits(int S_max, int Bc, int split_tiles) {

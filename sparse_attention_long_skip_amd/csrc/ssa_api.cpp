@@ -131,6 +131,27 @@ int check_sparge(const void* q, const void* k, int B, int H, int L, int d, int p
   return SSA_OK;
 }
 
+int check_vslash(const void* q, const void* k, int B, int H, int L, int d, int last_q, int n_vertical,
+                 int n_slash, int pool, int causal, const int32_t* block_idx,
+                 const int32_t* block_cnt, int max_blocks, const void* ws, size_t ws_bytes) {
+  if (!q || !k || !block_idx || !block_cnt) return SSA_ERR_INVALID_ARG;
+  if (B <= 0 || H <= 0 || L <= 0 || d <= 0 || pool <= 0) return SSA_ERR_INVALID_ARG;
+  if (last_q < 1 || last_q > L || n_vertical < 0 || n_slash < 0) return SSA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return SSA_ERR_INVALID_ARG;
+  if (!sizes_ok({B, H, L, d})) return SSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(block_idx, 4) || !aligned(block_cnt, 4))
+    return SSA_ERR_INVALID_ARG;
+  const long long nB = ((long long)L + pool - 1) / pool;
+  if (max_blocks < nB) return SSA_ERR_INVALID_ARG;
+  if (!causal) return SSA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return SSA_ERR_UNSUPPORTED;
+  if (pool != 64 || last_q > 64) return SSA_ERR_UNSUPPORTED;
+  if (nB > kMaxMaskBlocks || (long long)B * H > 65535) return SSA_ERR_UNSUPPORTED;
+  if (!ws || !aligned(ws, 256)) return SSA_ERR_WORKSPACE;
+  if (ws_bytes < ssa::VsWorkspace(B, H, L).total) return SSA_ERR_WORKSPACE;
+  return SSA_OK;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? SSA_OK : SSA_ERR_HIP; }
 
 }  // namespace
@@ -342,6 +363,40 @@ int ssa_block_mask_compressed(const void* q, const void* k, int B, int H, int L,
   p.workspace = workspace;
   p.compressed = 1;
   return hip_status(ssa::launch_block_mask(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t ssa_vertical_slash_workspace_size(int B, int H, int L) {
+  if (B <= 0 || H <= 0 || L <= 0) return 0;
+  return ssa::VsWorkspace(B, H, L).total;
+}
+
+int ssa_vertical_slash_mask(const void* q, const void* k, int B, int H, int L, int d, int last_q,
+                            int n_vertical, int n_slash, int pool, int causal, int32_t* block_idx,
+                            int32_t* block_cnt, int max_blocks, int32_t* vertical_idx,
+                            int32_t* slash_idx, float* vertical_scores, float* slash_scores,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_vslash(q, k, B, H, L, d, last_q, n_vertical, n_slash, pool, causal,
+                              block_idx, block_cnt, max_blocks, workspace, workspace_bytes);
+  if (st != SSA_OK) return st;
+  ssa::VsParams p = {};
+  p.q = q;
+  p.k = k;
+  p.B = B;
+  p.H = H;
+  p.L = L;
+  p.d = d;
+  p.last_q = last_q;
+  p.n_vertical = n_vertical;
+  p.n_slash = n_slash;
+  p.block_idx = block_idx;
+  p.block_cnt = block_cnt;
+  p.max_blocks = max_blocks;
+  p.vertical_idx = vertical_idx;
+  p.slash_idx = slash_idx;
+  p.vertical_scores = vertical_scores;
+  p.slash_scores = slash_scores;
+  p.workspace = workspace;
+  return hip_status(ssa::launch_vertical_slash(p, static_cast<hipStream_t>(stream)));
 }
 
 float ssa_lambda_from_scale_factor(float scale_factor, int L) {

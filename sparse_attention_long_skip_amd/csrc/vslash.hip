@@ -1,0 +1,422 @@
+// Vertical-slash block estimator for gfx950.
+//
+// Operation (MInference page: the vertical-slash pattern is estimated by
+// attending from the last query vector(s) to every key, which gives the best
+// vertical lines -- key columns -- and slash lines -- diagonals; its
+// vertical_slash_sparse_attention(q, k, v, vertical_topk, slash) call):
+//   rows i < R of the last R queries (positions p_i = L - R + i) attend
+//   causally, A[i, j] = softmax_{j <= p_i}(q_i . k_j / sqrt(d));
+//   v[j] = sum_i A[i, j]; s[o] = sum_i A[i, p_i - o];
+//   the n_vertical best keys and n_slash best offsets are chosen (ties: lower
+//   index first), and every 64 x 64 tile (b, c <= b) that holds an allowed
+//   entry on a chosen line is listed for the block-sparse prefill.
+//
+// Kernels, one launch each:
+//   (1) vs_pass<D, 0>: per chunk of 256 keys, S^T = K Q^T on 32x32x16 bf16
+//       MFMA (keys from HBM as the A operand, the R <= 64 query rows held as
+//       the B operand), online per-row (max, sum) partials in log2 units;
+//   (2) vs_rowstats: per-row max and 1/sum over the chunks;
+//   (3) vs_pass<D, 1>: recompute the chunk's scores, A into an LDS tile, then
+//       column sums (v, complete) and diagonal sums (partial at the chunk's
+//       edges) per chunk;
+//   (4) vs_slash_combine: s[o] from the at most two chunks holding offset o,
+//       in chunk order (deterministic);
+//   (5) vs_select: one workgroup per (line kind, head): the n-th largest score
+//       by a 32-round radix descent on block-wide counts, ties resolved by
+//       index with a block scan; emits per-tile vertical flags, the prefix
+//       count of chosen offsets and, optionally, the sorted index lists;
+//   (6) vs_cover: one wave per query tile tests every causal key tile with
+//       the flags and prefix counts and compacts the list with ballots.
+#include "common.h"
+#include "launch.h"
+
+namespace ssa {
+
+namespace {
+
+constexpr int CH = kVsChunk;    // keys per chunk (pass kernels)
+constexpr int SPW = kVsSpw;     // stride of the per-chunk diagonal partials
+constexpr int TILE = 64;        // block-sparse tile (Br = Bc)
+constexpr int SEL_T = 1024;     // threads of the selection kernel
+
+struct VsArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  int B, H, L, R, nchunk, nB, n_vert, n_slash, max_blocks;
+  float c_log2;  // log2(e) / sqrt(d)
+  float* part;   // [B, H, nchunk, 64, 2] (max, sum) in log2 units
+  float* stats;  // [B, H, 64, 2] (max, 1 / sum)
+  float* v;      // [B, H, L]
+  float* s;      // [B, H, L]
+  float* spart;  // [B, H, nchunk, SPW]
+  int32_t* vt;   // [B, H, nB] tile holds a chosen vertical
+  int32_t* P;    // [B, H, L + 1] chosen offsets below o
+  int32_t* block_idx;
+  int32_t* block_cnt;
+  int32_t* vert_idx;   // nullable [B, H, n_vert]
+  int32_t* slash_idx;  // nullable [B, H, n_slash]
+  float* v_out;        // nullable [B, H, L]
+  float* s_out;        // nullable [B, H, L]
+};
+
+__device__ __forceinline__ uint32_t order_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int D, int PASS>
+__global__ __launch_bounds__(256) void vs_pass(VsArgs a) {
+  constexpr int KS = D / 16;  // MFMA k-steps
+  __shared__ float A_lds[PASS ? 64 : 1][CH + 1];
+  __shared__ float red[4][64][2];
+  const int chunk = blockIdx.x;
+  const size_t hb = (size_t)blockIdx.z * a.H + blockIdx.y;
+  const uint16_t* kp = a.k + hb * a.L * D;
+  const uint16_t* qp = a.q + hb * a.L * D;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wv = t >> 6;
+  const int h = lane >> 5;
+  const int col = lane & 31;
+  const int j0 = chunk * CH;
+
+  // B operand: query rows rb * 32 + col (zero beyond R), 16 d-elements per step.
+  bf16x8 qop[2][KS];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int i = rb * 32 + col;
+    const bool ok = i < a.R;
+    const uint16_t* row = qp + (size_t)(a.L - a.R + (ok ? i : 0)) * D + 8 * h;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qop[rb][s] = ok ? as_bf16x8(load16(row + 16 * s)) : bf16x8{};
+  }
+  float mrow[2] = {0.f, 0.f}, invl[2] = {0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+  if constexpr (PASS == 1) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int i = rb * 32 + col;
+      mrow[rb] = i < a.R ? a.stats[(hb * 64 + i) * 2] : 0.f;
+      invl[rb] = i < a.R ? a.stats[(hb * 64 + i) * 2 + 1] : 0.f;
+    }
+  }
+
+  for (int g = wv; g < CH / 32; g += 4) {
+    const int jk = j0 + g * 32 + col;  // this lane's key for the A operand
+    bf16x8 kop[KS];
+    const uint16_t* krow = kp + (size_t)(jk < a.L ? jk : 0) * D + 8 * h;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kop[s] = jk < a.L ? as_bf16x8(load16(krow + 16 * s)) : bf16x8{};
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      acc[0] = mfma32(kop[s], qop[0][s], acc[0]);
+      acc[1] = mfma32(kop[s], qop[1][s], acc[1]);
+    }
+    // lane holds query row rb * 32 + col; register r holds key
+    // g * 32 + 8 (r / 4) + 4 h + r % 4 of the chunk
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int i = rb * 32 + col;
+      const int p = a.L - a.R + i;
+      if constexpr (PASS == 0) {
+        float mx = m_run[rb];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + g * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+          if (i < a.R && j < a.L && j <= p) mx = fmaxf(mx, acc[rb][r] * a.c_log2);
+        }
+        if (mx != -INFINITY) {
+          float l = m_run[rb] == -INFINITY ? 0.f : l_run[rb] * fast_exp2(m_run[rb] - mx);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = j0 + g * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+            if (i < a.R && j < a.L && j <= p) l += fast_exp2(acc[rb][r] * a.c_log2 - mx);
+          }
+          m_run[rb] = mx;
+          l_run[rb] = l;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jl = g * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+          const int j = j0 + jl;
+          const bool ok = i < a.R && j < a.L && j <= p;
+          A_lds[i][jl] = ok ? fast_exp2(acc[rb][r] * a.c_log2 - mrow[rb]) * invl[rb] : 0.f;
+        }
+      }
+    }
+  }
+
+  if constexpr (PASS == 0) {
+    // the two lanes of a row (h = 0, 1), then the four waves
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float mo = __shfl_xor(m_run[rb], 32, kWave);
+      const float lo = __shfl_xor(l_run[rb], 32, kWave);
+      const float mx = fmaxf(m_run[rb], mo);
+      float l = 0.f;
+      if (mx != -INFINITY) {
+        if (m_run[rb] != -INFINITY) l += l_run[rb] * fast_exp2(m_run[rb] - mx);
+        if (mo != -INFINITY) l += lo * fast_exp2(mo - mx);
+      }
+      if (h == 0) {
+        red[wv][rb * 32 + col][0] = mx;
+        red[wv][rb * 32 + col][1] = l;
+      }
+    }
+    __syncthreads();
+    if (t < 64) {
+      float mx = -INFINITY;
+      for (int w = 0; w < 4; ++w) mx = fmaxf(mx, red[w][t][0]);
+      float l = 0.f;
+      if (mx != -INFINITY)
+        for (int w = 0; w < 4; ++w)
+          if (red[w][t][0] != -INFINITY) l += red[w][t][1] * fast_exp2(red[w][t][0] - mx);
+      float* o = a.part + ((hb * a.nchunk + chunk) * 64 + t) * 2;
+      o[0] = mx;
+      o[1] = l;
+    }
+  } else {
+  __syncthreads();
+  // column sums: complete for this chunk's keys
+  {
+    const int j = j0 + t;
+    if (j < a.L) {
+      float sum = 0.f;
+      for (int i = 0; i < a.R; ++i) sum += A_lds[i][t];
+      a.v[hb * a.L + j] = sum;
+    }
+  }
+  // diagonal sums: offset o = L - R - (j0 + CH - 1) + e meets row i at chunk
+  // column i + CH - 1 - e
+  for (int e = t; e < CH + a.R - 1; e += 256) {
+    const int i0 = max(0, e - CH + 1);
+    const int i1 = min(a.R - 1, e);
+    float sum = 0.f;
+    for (int i = i0; i <= i1; ++i) sum += A_lds[i][i + CH - 1 - e];
+    a.spart[(hb * a.nchunk + chunk) * SPW + e] = sum;
+  }
+  }
+}
+
+__global__ __launch_bounds__(64) void vs_rowstats(VsArgs a) {
+  const size_t hb = (size_t)blockIdx.y * a.H + blockIdx.x;
+  const int i = threadIdx.x;
+  if (i >= a.R) return;
+  float mx = -INFINITY;
+  for (int c = 0; c < a.nchunk; ++c) mx = fmaxf(mx, a.part[((hb * a.nchunk + c) * 64 + i) * 2]);
+  float l = 0.f;
+  for (int c = 0; c < a.nchunk; ++c) {
+    const float* p = a.part + ((hb * a.nchunk + c) * 64 + i) * 2;
+    if (p[0] != -INFINITY) l += p[1] * fast_exp2(p[0] - mx);
+  }
+  a.stats[(hb * 64 + i) * 2] = mx;
+  a.stats[(hb * 64 + i) * 2 + 1] = 1.f / l;  // l >= 1: the row's own max term
+}
+
+__global__ __launch_bounds__(256) void vs_slash_combine(VsArgs a) {
+  const size_t hb = (size_t)blockIdx.z * a.H + blockIdx.y;
+  const int o = blockIdx.x * 256 + threadIdx.x;
+  if (o >= a.L) return;
+  // chunk c holds offset o at e = y + c * CH, for 0 <= e < CH + R - 1
+  const int y = o - a.L + a.R + CH - 1;
+  int c = y >= 0 ? 0 : (-y + CH - 1) / CH;
+  float sum = 0.f;
+  for (; c < a.nchunk && y + c * CH < CH + a.R - 1; ++c)
+    sum += a.spart[(hb * a.nchunk + c) * SPW + (y + c * CH)];
+  a.s[hb * a.L + o] = sum;
+  if (a.s_out) a.s_out[hb * a.L + o] = sum;
+  if (a.v_out) a.v_out[hb * a.L + o] = a.v[hb * a.L + o];
+}
+
+// Block-wide sum of an int over SEL_T threads; every thread gets the total.
+__device__ int block_sum(int x, int* scratch) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
+  __syncthreads();  // scratch reuse
+  if (lane == 0) scratch[w] = x;
+  __syncthreads();
+  int tot = 0;
+#pragma unroll
+  for (int i = 0; i < SEL_T / 64; ++i) tot += scratch[i];
+  return tot;
+}
+
+// Block-wide exclusive prefix sum over thread order.
+__device__ int block_exclusive_scan(int x, int* scratch) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  int inc = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += y;
+  }
+  __syncthreads();
+  if (lane == 63) scratch[w] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < w; ++i) before += scratch[i];
+  return before + inc - x;
+}
+
+__global__ __launch_bounds__(SEL_T) void vs_select(VsArgs a) {
+  __shared__ int scratch[SEL_T / 64];
+  const bool slash = blockIdx.x == 1;
+  const size_t hb = (size_t)blockIdx.z * a.H + blockIdx.y;
+  const float* x = (slash ? a.s : a.v) + hb * a.L;
+  const int n = slash ? a.n_slash : a.n_vert;
+  const int L = a.L;
+  const int t = threadIdx.x;
+
+  // the n-th largest key T: largest value with #{u >= T} >= n
+  uint32_t thr = 0;
+  const bool take_all = n >= L;
+  if (n > 0 && !take_all) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      int c = 0;
+      for (int j = t; j < L; j += SEL_T) c += order_bits(x[j]) >= cand;
+      if (block_sum(c, scratch) >= n) thr = cand;
+    }
+  }
+  int gt = 0;
+  if (n > 0 && !take_all)
+    for (int j = t; j < L; j += SEL_T) gt += order_bits(x[j]) > thr;
+  const int need_eq = (n > 0 && !take_all) ? n - block_sum(gt, scratch) : 0;
+
+  // thread t owns [t * per, (t + 1) * per), per a multiple of the tile
+  const int per = ((L + SEL_T - 1) / SEL_T + TILE - 1) / TILE * TILE;
+  const int lo = min(L, t * per);
+  const int hi = min(L, lo + per);
+  auto chosen_raw = [&](int j) -> int {  // 2: above T, 1: equal to T, 0: no
+    if (take_all) return 2;
+    if (n <= 0) return 0;
+    const uint32_t u = order_bits(x[j]);
+    return u > thr ? 2 : (u == thr ? 1 : 0);
+  };
+  int eq = 0;
+  for (int j = lo; j < hi; ++j) eq += chosen_raw(j) == 1;
+  const int eq_before = block_exclusive_scan(eq, scratch);
+  int cnt = 0;
+  {
+    int e = eq_before;
+    for (int j = lo; j < hi; ++j) {
+      const int c = chosen_raw(j);
+      if (c == 2 || (c == 1 && e++ < need_eq)) ++cnt;
+    }
+  }
+  const int sel_before = block_exclusive_scan(cnt, scratch);
+  int32_t* list = slash ? a.slash_idx : a.vert_idx;
+  const int nlist = slash ? a.n_slash : a.n_vert;
+  int e = eq_before, k = sel_before;
+  int tile_any = 0;
+  for (int j = lo; j < hi; ++j) {
+    const int c = chosen_raw(j);
+    const bool sel = c == 2 || (c == 1 && e++ < need_eq);
+    if (slash) a.P[hb * (L + 1) + j] = k;
+    if (sel) {
+      if (list && k < nlist) list[hb * nlist + k] = j;
+      ++k;
+      tile_any = 1;
+    }
+    if (!slash && ((j + 1) % TILE == 0 || j + 1 == hi)) {
+      a.vt[hb * a.nB + j / TILE] = tile_any;
+      tile_any = 0;
+    }
+  }
+  if (slash && hi == L && lo < hi) a.P[hb * (L + 1) + L] = k;  // the thread holding key L - 1
+  // lists shorter than their length (n above L) are padded with -1
+  if (list && t == 0)
+    for (int r = min(n, L); r < nlist; ++r) list[hb * nlist + r] = -1;
+}
+
+__global__ __launch_bounds__(256) void vs_cover(VsArgs a) {
+  const size_t hb = (size_t)blockIdx.z * a.H + blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int qb = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (qb >= a.nB) return;
+  const int L = a.L;
+  const int r_lo = qb * TILE;
+  const int r_hi = min(L - 1, r_lo + TILE - 1);
+  const int32_t* P = a.P + hb * (L + 1);
+  const int32_t* vt = a.vt + hb * a.nB;
+  int32_t* out = a.block_idx + (hb * a.nB + qb) * a.max_blocks;
+  int base = 0;
+  for (int c0 = 0; c0 <= qb; c0 += 64) {
+    const int c = c0 + lane;
+    bool kept = false;
+    if (c <= qb) {
+      const int j_lo = c * TILE;
+      const int j_hi = min(L - 1, j_lo + TILE - 1);
+      const int lo = max(0, r_lo - j_hi);
+      const int hi = r_hi - j_lo;  // <= L - 1
+      kept = vt[c] != 0 || P[hi + 1] - P[lo] > 0;
+    }
+    const uint64_t bal = __ballot(kept);
+    if (kept) out[base + __popcll(bal & ((1ull << lane) - 1ull))] = c;
+    base += __popcll(bal);
+  }
+  for (int r = base + lane; r < a.max_blocks; r += 64) out[r] = -1;
+  if (lane == 0) a.block_cnt[hb * a.nB + qb] = base;
+}
+
+template <int D>
+hipError_t launch(const VsArgs& a, hipStream_t stream) {
+  const dim3 g_pass(a.nchunk, a.H, a.B);
+  hipLaunchKernelGGL((vs_pass<D, 0>), g_pass, dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(vs_rowstats, dim3(a.H, a.B), dim3(64), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((vs_pass<D, 1>), g_pass, dim3(256), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(vs_slash_combine, dim3((a.L + 255) / 256, a.H, a.B), dim3(256), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(vs_select, dim3(2, a.H, a.B), dim3(SEL_T), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(vs_cover, dim3((a.nB + 3) / 4, a.H, a.B), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_vertical_slash(const VsParams& p, hipStream_t stream) {
+  VsArgs a = {};
+  a.q = static_cast<const uint16_t*>(p.q);
+  a.k = static_cast<const uint16_t*>(p.k);
+  a.B = p.B;
+  a.H = p.H;
+  a.L = p.L;
+  a.R = p.last_q;
+  a.nchunk = (p.L + CH - 1) / CH;
+  a.nB = (p.L + TILE - 1) / TILE;
+  a.n_vert = p.n_vertical;
+  a.n_slash = p.n_slash;
+  a.max_blocks = p.max_blocks;
+  a.c_log2 = 1.4426950408889634f / sqrtf((float)p.d);
+  VsWorkspace w(p.B, p.H, p.L);
+  char* base = static_cast<char*>(p.workspace);
+  a.part = reinterpret_cast<float*>(base + w.part);
+  a.stats = reinterpret_cast<float*>(base + w.stats);
+  a.v = reinterpret_cast<float*>(base + w.v);
+  a.s = reinterpret_cast<float*>(base + w.s);
+  a.spart = reinterpret_cast<float*>(base + w.spart);
+  a.vt = reinterpret_cast<int32_t*>(base + w.vt);
+  a.P = reinterpret_cast<int32_t*>(base + w.P);
+  a.block_idx = p.block_idx;
+  a.block_cnt = p.block_cnt;
+  a.vert_idx = p.vertical_idx;
+  a.slash_idx = p.slash_idx;
+  a.v_out = p.vertical_scores;
+  a.s_out = p.slash_scores;
+  if (p.d == 128) return launch<128>(a, stream);
+  if (p.d == 64) return launch<64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ssa

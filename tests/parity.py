@@ -275,3 +275,65 @@ def sparge_parity(q_bits, k_bits, theta, tau, mode="mass", pool=64, heads=None):
                 assert len(set(got) ^ set(want)) <= 2, (b, h, qb)
             n_near += 1
     return {"near": n_near, "gpu": g, "refs": refs}
+
+
+def _near_kth(x, kth, rel=1e-5):
+    return np.abs(x - kth) <= rel * abs(kth) + 1e-9
+
+
+def vslash_parity(q_bits, k_bits, last_q, n_vertical, n_slash, heads=None, pool=64):
+    """HIP vertical-slash estimator vs the oracle on the listed (b, h) heads.
+
+    Scores v, s must agree to fp32 accuracy. The chosen keys / offsets must
+    match except entries whose oracle score lies within a relative 1e-5 of
+    the n-th score (near-ties: the GPU ranks fp32 sums, the oracle fp64).
+    Heads whose chosen sets match must produce exactly the oracle's tile
+    lists; heads with a near-tie difference are counted and their lists
+    checked for shape only."""
+    import sparse_attention_long_skip_amd as ssa
+    q, k = dev_bf16(q_bits), dev_bf16(k_bits)
+    g = ssa.vertical_slash_mask(q, k, n_vertical, n_slash, last_q, pool, indices=True, scores=True)
+    torch.cuda.synchronize()
+    B, H, L, d = q_bits.shape
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+    gi, gc = to_np(g["block_idx"]), to_np(g["block_cnt"])
+    gv, gs = to_np(g["v"]), to_np(g["s"])
+    gvert = to_np(g["vertical"]) if n_vertical > 0 else None
+    gsl = to_np(g["slash"]) if n_slash > 0 else None
+    n_tie_heads = 0
+    refs = {}
+    for (b, h) in heads:
+        r = oracle.vertical_slash_mask(q_bits[b:b + 1, h:h + 1], k_bits[b:b + 1, h:h + 1], last_q,
+                                       n_vertical, n_slash, pool, bits=True)
+        refs[(b, h)] = r
+        v, s = r["v"][0, 0], r["s"][0, 0]
+        np.testing.assert_allclose(gv[b, h], v, rtol=1e-4, atol=1e-6)
+        np.testing.assert_allclose(gs[b, h], s, rtol=1e-4, atol=1e-6)
+        same = True
+        for name, got_all, want, x, kth, n in (
+                ("vertical", gvert, r["vertical"][(0, 0)], v, r["v_kth"][0, 0], n_vertical),
+                ("slash", gsl, r["slash"][(0, 0)], s, r["s_kth"][0, 0], n_slash)):
+            if n == 0:
+                continue
+            got = got_all[b, h]
+            m = min(n, L)
+            assert np.all(got[m:] == -1)
+            got = got[:m]
+            assert np.all(np.diff(got) > 0), name
+            diff = set(got.tolist()) ^ set(want.tolist())
+            if diff:
+                assert all(_near_kth(x[j], kth) for j in diff), (name, b, h, sorted(diff)[:8])
+                same = False
+        nB = r["block_cnt"].shape[-1]
+        for qb in range(nB):
+            row = gi[b, h, qb]
+            assert np.all(row[gc[b, h, qb]:] == -1)
+            lst = row[:gc[b, h, qb]]
+            assert np.all(np.diff(lst) > 0) and (len(lst) == 0 or (lst[0] >= 0 and lst[-1] <= qb))
+        if same:
+            np.testing.assert_array_equal(gc[b, h], r["block_cnt"][0, 0])
+            np.testing.assert_array_equal(gi[b, h], r["block_idx"][0, 0])
+        else:
+            n_tie_heads += 1
+    return {"tie_heads": n_tie_heads, "gpu": g, "refs": refs}

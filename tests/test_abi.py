@@ -174,3 +174,27 @@ def test_compressed_mask_validation(lib):
     need = lib.ssa_block_mask_compressed_workspace_size(1, 2, 32768, 64, 64)
     assert need == 2 * (512 + 2048) * 64 * 4
     assert call(wsb=need - 1) == -3
+
+
+def test_vertical_slash_validation(lib):
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, B=1, H=2, L=32768, d=64, R=64, nv=1000, ns=64, pool=64, causal=1,
+                 bi=FAKE, bc=FAKE, mb=512, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.ssa_vertical_slash_mask(a["q"], a["k"], a["B"], a["H"], a["L"], a["d"], a["R"],
+                                           a["nv"], a["ns"], a["pool"], a["causal"], a["bi"], a["bc"],
+                                           a["mb"], None, None, None, None, a["ws"], a["wsb"], None)
+    assert call(q=None) == -1
+    assert call(R=0) == -1
+    assert call(R=40000) == -1
+    assert call(nv=-1) == -1
+    assert call(ns=-2) == -1
+    assert call(mb=511) == -1
+    assert call(R=65) == -2
+    assert call(pool=32, mb=1024) == -2
+    assert call(d=96) == -2
+    assert call(causal=0) == -2
+    assert call(ws=None) == -3
+    need = lib.ssa_vertical_slash_workspace_size(1, 2, 32768)
+    assert need > 2 * 2 * 32768 * 4
+    assert call(wsb=need - 1) == -3
