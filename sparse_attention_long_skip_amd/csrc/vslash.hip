@@ -22,8 +22,8 @@
 //   (4) vs_slash_combine: s[o] from the at most two chunks holding offset o,
 //       in chunk order (deterministic);
 //   (5) vs_select: one workgroup per (line kind, head): the n-th largest score
-//       by a 32-round radix descent on block-wide counts, ties resolved by
-//       index with a block scan; emits per-tile vertical flags, the prefix
+//       by a 4-pass radix select on 8-bit digits (LDS histogram, block scan),
+//       ties resolved by index with a block scan; emits per-tile vertical flags, the prefix
 //       count of chosen offsets and, optionally, the sorted index lists;
 //   (6) vs_cover: one wave per query tile tests every causal key tile with
 //       the flags and prefix counts and compacts the list with ballots.
@@ -201,19 +201,35 @@ __global__ __launch_bounds__(256) void vs_pass(VsArgs a) {
   }
 }
 
-__global__ __launch_bounds__(64) void vs_rowstats(VsArgs a) {
+// Row statistics over the chunks: 16 slices of chunks per row, combined in LDS.
+__global__ __launch_bounds__(1024) void vs_rowstats(VsArgs a) {
+  constexpr int NSL = 16;
+  __shared__ float red[NSL][64][2];
   const size_t hb = (size_t)blockIdx.y * a.H + blockIdx.x;
-  const int i = threadIdx.x;
-  if (i >= a.R) return;
-  float mx = -INFINITY;
-  for (int c = 0; c < a.nchunk; ++c) mx = fmaxf(mx, a.part[((hb * a.nchunk + c) * 64 + i) * 2]);
-  float l = 0.f;
-  for (int c = 0; c < a.nchunk; ++c) {
-    const float* p = a.part + ((hb * a.nchunk + c) * 64 + i) * 2;
-    if (p[0] != -INFINITY) l += p[1] * fast_exp2(p[0] - mx);
+  const int i = threadIdx.x & 63;
+  const int sl = threadIdx.x >> 6;
+  float mx = -INFINITY, l = 0.f;
+  if (i < a.R) {
+    for (int c = sl; c < a.nchunk; c += NSL) {
+      const float* p = a.part + ((hb * a.nchunk + c) * 64 + i) * 2;
+      const float pm = p[0], pl = p[1];
+      if (pm == -INFINITY) continue;
+      const float m2 = fmaxf(mx, pm);
+      l = (mx == -INFINITY ? 0.f : l * fast_exp2(mx - m2)) + pl * fast_exp2(pm - m2);
+      mx = m2;
+    }
   }
-  a.stats[(hb * 64 + i) * 2] = mx;
-  a.stats[(hb * 64 + i) * 2 + 1] = 1.f / l;  // l >= 1: the row's own max term
+  red[sl][i][0] = mx;
+  red[sl][i][1] = l;
+  __syncthreads();
+  if (sl != 0 || i >= a.R) return;
+  float m = -INFINITY;
+  for (int k = 0; k < NSL; ++k) m = fmaxf(m, red[k][i][0]);
+  float tot = 0.f;
+  for (int k = 0; k < NSL; ++k)
+    if (red[k][i][0] != -INFINITY) tot += red[k][i][1] * fast_exp2(red[k][i][0] - m);
+  a.stats[(hb * 64 + i) * 2] = m;
+  a.stats[(hb * 64 + i) * 2 + 1] = 1.f / tot;  // tot >= 1: the row's own max term
 }
 
 __global__ __launch_bounds__(256) void vs_slash_combine(VsArgs a) {
@@ -229,21 +245,6 @@ __global__ __launch_bounds__(256) void vs_slash_combine(VsArgs a) {
   a.s[hb * a.L + o] = sum;
   if (a.s_out) a.s_out[hb * a.L + o] = sum;
   if (a.v_out) a.v_out[hb * a.L + o] = a.v[hb * a.L + o];
-}
-
-// Block-wide sum of an int over SEL_T threads; every thread gets the total.
-__device__ int block_sum(int x, int* scratch) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
-  __syncthreads();  // scratch reuse
-  if (lane == 0) scratch[w] = x;
-  __syncthreads();
-  int tot = 0;
-#pragma unroll
-  for (int i = 0; i < SEL_T / 64; ++i) tot += scratch[i];
-  return tot;
 }
 
 // Block-wide exclusive prefix sum over thread order.
@@ -264,8 +265,34 @@ __device__ int block_exclusive_scan(int x, int* scratch) {
   return before + inc - x;
 }
 
+// Block-wide exclusive prefix sum of 64-bit values; *total gets the sum of all.
+__device__ uint64_t block_exclusive_scan64(uint64_t x, uint64_t* scratch, uint64_t* total) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  uint64_t inc = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t lo = __shfl_up((uint32_t)inc, o, kWave);
+    const uint32_t hi = __shfl_up((uint32_t)(inc >> 32), o, kWave);
+    if (lane >= o) inc += ((uint64_t)hi << 32) | lo;
+  }
+  __syncthreads();
+  if (lane == 63) scratch[w] = inc;
+  __syncthreads();
+  uint64_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < SEL_T / 64; ++i) {
+    const uint64_t v = scratch[i];
+    before += i < w ? v : 0ull;
+    all += v;
+  }
+  *total = all;
+  return before + inc - x;
+}
+
 __global__ __launch_bounds__(SEL_T) void vs_select(VsArgs a) {
   __shared__ int scratch[SEL_T / 64];
+  __shared__ uint64_t scratch64[SEL_T / 64];
   const bool slash = blockIdx.x == 1;
   const size_t hb = (size_t)blockIdx.z * a.H + blockIdx.y;
   const float* x = (slash ? a.s : a.v) + hb * a.L;
@@ -273,66 +300,132 @@ __global__ __launch_bounds__(SEL_T) void vs_select(VsArgs a) {
   const int L = a.L;
   const int t = threadIdx.x;
 
-  // the n-th largest key T: largest value with #{u >= T} >= n
-  uint32_t thr = 0;
+  // The n-th largest key T, 8 bits at a time: per pass, a histogram of the
+  // next digit over the keys that match the digits found so far, then the
+  // largest digit whose suffix count reaches the rank still needed. After
+  // the last pass `need` is how many keys equal to T are taken.
+  // 16 copies of the histogram (by lane % 16, rows padded to spread banks)
+  // so that keys sharing a digit do not all hit one LDS address.
+  constexpr int NCOPY = 16, HS = 257;
+  __shared__ int hist[NCOPY * HS];
+  __shared__ int pick[2];
+  uint32_t thr = 0, mask = 0;
+  int need = n;
   const bool take_all = n >= L;
-  if (n > 0 && !take_all) {
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = thr | (1u << bit);
-      int c = 0;
-      for (int j = t; j < L; j += SEL_T) c += order_bits(x[j]) >= cand;
-      if (block_sum(c, scratch) >= n) thr = cand;
+  const bool by_rank = n > 0 && !take_all;
+  if (by_rank) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int e = t; e < NCOPY * HS; e += SEL_T) hist[e] = 0;
+      __syncthreads();
+      int* mine = hist + (t & (NCOPY - 1)) * HS;
+      for (int b0 = 0; b0 < L; b0 += SEL_T * 8) {  // 8 loads in flight per thread
+        uint32_t u[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = b0 + e * SEL_T + t;
+          u[e] = j < L ? order_bits(x[j]) : 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = b0 + e * SEL_T + t;
+          if (j < L && (u[e] & mask) == thr) atomicAdd(&mine[(u[e] >> shift) & 255], 1);
+        }
+      }
+      __syncthreads();
+      // thread t looks at digit 255 - t: suffix count S = excl + own
+      int own = 0;
+      if (t < 256)
+        for (int cpy = 0; cpy < NCOPY; ++cpy) own += hist[cpy * HS + 255 - t];
+      const int excl = block_exclusive_scan(own, scratch);
+      if (t < 256 && excl < need && excl + own >= need) {
+        pick[0] = 255 - t;
+        pick[1] = need - excl;
+      }
+      __syncthreads();
+      thr |= (uint32_t)pick[0] << shift;
+      mask |= 255u << shift;
+      need = pick[1];
+      __syncthreads();  // pick is rewritten next pass
     }
   }
-  int gt = 0;
-  if (n > 0 && !take_all)
-    for (int j = t; j < L; j += SEL_T) gt += order_bits(x[j]) > thr;
-  const int need_eq = (n > 0 && !take_all) ? n - block_sum(gt, scratch) : 0;
+  const int need_eq = by_rank ? need : 0;
 
-  // thread t owns [t * per, (t + 1) * per), per a multiple of the tile
-  const int per = ((L + SEL_T - 1) / SEL_T + TILE - 1) / TILE * TILE;
-  const int lo = min(L, t * per);
-  const int hi = min(L, lo + per);
-  auto chosen_raw = [&](int j) -> int {  // 2: above T, 1: equal to T, 0: no
-    if (take_all) return 2;
-    if (n <= 0) return 0;
-    const uint32_t u = order_bits(x[j]);
-    return u > thr ? 2 : (u == thr ? 1 : 0);
-  };
-  int eq = 0;
-  for (int j = lo; j < hi; ++j) eq += chosen_raw(j) == 1;
-  const int eq_before = block_exclusive_scan(eq, scratch);
-  int cnt = 0;
-  {
-    int e = eq_before;
-    for (int j = lo; j < hi; ++j) {
-      const int c = chosen_raw(j);
-      if (c == 2 || (c == 1 && e++ < need_eq)) ++cnt;
-    }
-  }
-  const int sel_before = block_exclusive_scan(cnt, scratch);
+  // Ordered sweep over steps of SEL_T * PER keys, PER consecutive keys per
+  // thread (the next step's keys are loaded before this step's scan): a key
+  // above T is taken, a key equal to T is taken while fewer than need_eq
+  // equal keys precede it. One block scan of the packed (above, equal)
+  // counts per step gives each key's rank. A wave covers 4 tiles of 64 keys
+  // (16 lanes each).
+  constexpr int PER = 4;
+  constexpr int STEP = SEL_T * PER;
   int32_t* list = slash ? a.slash_idx : a.vert_idx;
   const int nlist = slash ? a.n_slash : a.n_vert;
-  int e = eq_before, k = sel_before;
-  int tile_any = 0;
-  for (int j = lo; j < hi; ++j) {
-    const int c = chosen_raw(j);
-    const bool sel = c == 2 || (c == 1 && e++ < need_eq);
-    if (slash) a.P[hb * (L + 1) + j] = k;
-    if (sel) {
-      if (list && k < nlist) list[hb * nlist + k] = j;
-      ++k;
-      tile_any = 1;
+  int32_t* P = a.P + hb * (L + 1);
+  auto load_step = [&](int base, float* o) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int j = base + PER * t + e;
+      o[e] = (by_rank && j < L) ? x[j] : 0.f;
     }
-    if (!slash && ((j + 1) % TILE == 0 || j + 1 == hi)) {
-      a.vt[hb * a.nB + j / TILE] = tile_any;
-      tile_any = 0;
+  };
+  float xv[PER], xn[PER];
+  load_step(0, xv);
+  uint64_t run = 0;  // (above << 32) | equal, over the keys before this step
+  for (int base = 0; base < L; base += STEP) {
+    if (base + STEP < L) load_step(base + STEP, xn);
+    int cc[PER];  // 2: above T, 1: equal to T, 0: not taken
+    uint64_t mine = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int j = base + PER * t + e;
+      int c = 0;
+      if (j < L) {
+        if (take_all) {
+          c = 2;
+        } else if (by_rank) {
+          const uint32_t u = order_bits(xv[e]);
+          c = u > thr ? 2 : (u == thr ? 1 : 0);
+        }
+      }
+      cc[e] = c;
+      mine += c == 2 ? (1ull << 32) : (uint64_t)(c == 1);
     }
+    uint64_t total;
+    uint64_t acc = run + block_exclusive_scan64(mine, scratch64, &total);
+    run += total;
+    bool any = false;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int j = base + PER * t + e;
+      const int gt_before = (int)(acc >> 32);
+      const int eq_before = (int)(acc & 0xffffffffu);
+      const bool sel = cc[e] == 2 || (cc[e] == 1 && eq_before < need_eq);
+      const int pos = gt_before + min(eq_before, need_eq);
+      if (j < L) {
+        if (slash) P[j] = pos;
+        if (sel && list && pos < nlist) list[hb * nlist + pos] = j;
+      }
+      any |= sel;
+      acc += cc[e] == 2 ? (1ull << 32) : (uint64_t)(cc[e] == 1);
+    }
+    if (!slash) {
+      const uint64_t bal = __ballot(any);
+      if ((t & 63) == 0) {
+        const int tile0 = (base + (t >> 6) * 64 * PER) / TILE;
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+          if ((tile0 + q) * TILE < L) a.vt[hb * a.nB + tile0 + q] = ((bal >> (16 * q)) & 0xffffull) ? 1 : 0;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) xv[e] = xn[e];
   }
-  if (slash && hi == L && lo < hi) a.P[hb * (L + 1) + L] = k;  // the thread holding key L - 1
-  // lists shorter than their length (n above L) are padded with -1
-  if (list && t == 0)
-    for (int r = min(n, L); r < nlist; ++r) list[hb * nlist + r] = -1;
+  if (t == 0) {
+    const int taken = take_all ? L : (by_rank ? n : 0);
+    if (slash) P[L] = taken;
+    if (list)
+      for (int r = min(n, L); r < nlist; ++r) list[hb * nlist + r] = -1;  // n above L
+  }
 }
 
 __global__ __launch_bounds__(256) void vs_cover(VsArgs a) {
@@ -371,7 +464,7 @@ hipError_t launch(const VsArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((vs_pass<D, 0>), g_pass, dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(vs_rowstats, dim3(a.H, a.B), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(vs_rowstats, dim3(a.H, a.B), dim3(1024), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((vs_pass<D, 1>), g_pass, dim3(256), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
