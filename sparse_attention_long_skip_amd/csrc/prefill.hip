@@ -59,7 +59,8 @@ struct PrefillArgs {
   uint8_t* tile_state;
   float* tile_margin;
   int B, Hq, Hkv, L, nQ, nK, G;
-  int tasks, per_xcd;  // B*Hq*nQ work items; items per XCD
+  int tasks, per_xcd;  // B*Hq*nQ work items; workgroup slots per XCD
+  int xcd_rr;          // deal groups of G items round-robin over the XCDs
   float lam_raw;       // lambda * sqrt(d): threshold on raw q.k differences
   float c_log2;        // log2(e) / sqrt(d)
   float inv_sqrt_d;
@@ -104,11 +105,25 @@ void prefill_kernel(PrefillArgs a) {
   const int h = lane >> 5;
   const int r32 = lane & 31;
 
-  // XCD-aware work mapping: XCD x takes items [x*per_xcd, (x+1)*per_xcd).
+  // XCD-aware work mapping (workgroups are dealt to the XCDs round-robin by
+  // index). Items are ordered (batch, KV head), heaviest query tile first,
+  // the G heads of a tile adjacent. When the (batch, KV head) pairs divide
+  // evenly over the XCDs, XCD x takes the contiguous items
+  // [x*per_xcd, (x+1)*per_xcd): whole KV heads, so K/V stay in its L2.
+  // Otherwise the groups of G items (one query tile of one KV head) are
+  // dealt round-robin to the XCDs, which balances the causal work.
   const int xcd = blockIdx.x % kNumXcd;
   const int slot = blockIdx.x / kNumXcd;
-  const int task = xcd * a.per_xcd + slot;
-  if (slot >= a.per_xcd || task >= a.tasks) return;
+  int task;
+  if (a.xcd_rr) {
+    const int kq = slot / a.G;
+    const int grp = kq * kNumXcd + xcd;
+    if (grp >= a.tasks / a.G) return;
+    task = grp * a.G + (slot - kq * a.G);
+  } else {
+    task = xcd * a.per_xcd + slot;
+    if (slot >= a.per_xcd || task >= a.tasks) return;
+  }
   const int per_bkv = a.G * a.nQ;
   const int bkv = task / per_bkv;
   const int rem = task - bkv * per_bkv;
@@ -488,7 +503,13 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   a.nK = (p.L + p.Bc - 1) / p.Bc;
   a.G = p.Hq / p.Hkv;
   a.tasks = p.B * p.Hq * a.nQ;
-  a.per_xcd = (a.tasks + kNumXcd - 1) / kNumXcd;
+  a.xcd_rr = (p.B * p.Hkv) % kNumXcd != 0;
+  if (a.xcd_rr) {
+    const int groups = p.B * p.Hkv * a.nQ;
+    a.per_xcd = (groups + kNumXcd - 1) / kNumXcd * a.G;
+  } else {
+    a.per_xcd = (a.tasks + kNumXcd - 1) / kNumXcd;
+  }
   const float sd = sqrtf((float)p.d);
   a.lam_raw = p.lambda * sd;
   a.c_log2 = kLog2e / sd;
