@@ -69,8 +69,7 @@ struct PrefillArgs {
   const int32_t* block_cnt;
   int max_blocks;
   int nm_n, nm_m, dense_sink, dense_recent;  // N:M sparse softmax (NM instances)
-  int wave_vote;  // 1: every 32-row wave is its own decision unit (Br = 32)
-  int nQ_unit;    // decision units per (batch, head): nQ, or nQ * NW with wave_vote
+  int nQ_unit;    // decision units (query tiles of Br rows) per (batch, head)
 };
 
 // 16-byte chunk swizzles of a tile row (physical chunk = logical ^ swz(row)).
@@ -80,14 +79,19 @@ __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
-// STATS: write per-tile decisions / margins (a separate instance, so the hot
-// instance carries none of that code). SPARSE: visit a per-tile block list.
-// NM: N:M sparse softmax on the scores before the tile rule. WV: per-wave
-// decision units (Br = 32).
-template <int D, int BR, bool STATS, bool SPARSE, bool NM, bool WV>
-__global__ __launch_bounds__(BR * 2) __attribute__((amdgpu_waves_per_eu(2)))
+// BR: query rows per workgroup (BR / 32 waves). UW: waves per decision unit
+// (the query tile of Br = 32 * UW rows); a workgroup holds BR / (32 UW)
+// units that vote separately and share the K/V tiles (V is loaded when any
+// unit keeps the tile). STATS: write per-tile decisions / margins (a
+// separate instance, so the hot instance carries none of that code).
+// SPARSE: visit a per-tile block list (one unit per workgroup). NM: N:M
+// sparse softmax on the scores before the tile rule.
+template <int D, int BR, bool STATS, bool SPARSE, bool NM, int UW>
+__global__ __launch_bounds__(BR * 2) __attribute__((amdgpu_waves_per_eu(BR >= 256 ? 4 : 2)))
 void prefill_kernel(PrefillArgs a) {
   constexpr int NW = BR / 32;
+  constexpr int NU = NW / UW;  // decision units per workgroup
+  static_assert(NU * UW == NW && (!SPARSE || NU == 1), "unit layout");
   constexpr int NT = NW * kWave;
   constexpr int CPR = D / 8;                   // 16-byte chunks per row
   constexpr int TILE = BC * D;                 // bf16 elements per K or V tile
@@ -137,9 +141,14 @@ void prefill_kernel(PrefillArgs a) {
   const bool row_ok = row < L;
   const int last_row = min(q0 + BR, L) - 1;
   // This wave's rows: a tile none of them can see contributes nothing to
-  // them, so the wave skips its exponentials and P.V there.
+  // them, so the wave skips its exponentials and P.V there. Its decision
+  // unit u covers rows [q0 + 32 UW u, q0 + 32 UW (u + 1)).
   const bool wave_rows = q0 + w * 32 < L;
   const int wave_last = min(q0 + w * 32 + 31, L - 1);
+  const int u = w / UW;
+  const bool unit_rows = q0 + u * UW * 32 < L;
+  const int unit_last = min(q0 + (u + 1) * UW * 32 - 1, L - 1);
+  const size_t unit_id = (size_t)(b * a.Hq + hq) * a.nQ_unit + (size_t)i * NU + u;
 
   const uint16_t* qp = a.q + ((size_t)(b * a.Hq + hq) * L) * D;
   const uint16_t* kp = a.k + ((size_t)(b * a.Hkv + kvh) * L) * D;
@@ -302,41 +311,43 @@ void prefill_kernel(PrefillArgs a) {
     bool keep1 = false;  // this wave takes the exponentials and P.V of tile jprev
     if (have_prev) {
       // keep_any: some decision unit of the workgroup keeps the tile (V is
-      // loaded); keep_mine: this wave's unit keeps it.
+      // loaded); keep_mine: this wave's unit keeps it. A unit whose rows
+      // cannot see the tile (causal) does not count it as visited.
       bool keep_any, keep_mine;
-      const bool wvis = !WV || (wave_rows && (!a.causal || jprev * BC <= wave_last));
+      const bool wvis = wave_rows && (!a.causal || jprev * BC <= wave_last);
+      const bool uvis = unit_rows && (!a.causal || jprev * BC <= unit_last);
       if (STATS) {
-        float g = flag_lds[buf ^ 1][0];
+        float gu = flag_lds[buf ^ 1][u * UW];
 #pragma unroll
-        for (int ww = 1; ww < NW; ++ww) g = fmaxf(g, flag_lds[buf ^ 1][ww]);
+        for (int ww = 1; ww < UW; ++ww) gu = fmaxf(gu, flag_lds[buf ^ 1][u * UW + ww]);
+        float g = gu;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) g = fmaxf(g, flag_lds[buf ^ 1][ww]);
         keep_any = !(g < a.lam_raw);
-        const float gw = flag_lds[buf ^ 1][w];
-        keep_mine = WV ? !(gw < a.lam_raw) : keep_any;
-        if (WV) {
-          if (lane == 0 && wvis) {
-            const size_t ti = (((size_t)(b * a.Hq + hq) * a.nQ_unit) + i * NW + w) * a.nK + jprev;
-            if (a.tile_state) a.tile_state[ti] = keep_mine ? 1 : 2;
-            if (a.tile_margin) a.tile_margin[ti] = gw * a.inv_sqrt_d;
-          }
-        } else if (tid == 0) {
-          const size_t ti = unit * a.nK + jprev;
-          if (a.tile_state) a.tile_state[ti] = keep_any ? 1 : 2;
-          if (a.tile_margin) a.tile_margin[ti] = g * a.inv_sqrt_d;
+        keep_mine = !(gu < a.lam_raw);
+        if (lane == 0 && w % UW == 0 && uvis) {
+          const size_t ti = unit_id * a.nK + jprev;
+          if (a.tile_state) a.tile_state[ti] = keep_mine ? 1 : 2;
+          if (a.tile_margin) a.tile_margin[ti] = gu * a.inv_sqrt_d;
         }
       } else {
-        float f = flag_lds[buf ^ 1][0];
+        float fu = 0.f, f = 0.f;
 #pragma unroll
-        for (int ww = 1; ww < NW; ++ww) f += flag_lds[buf ^ 1][ww];
+        for (int ww = 0; ww < NW; ++ww) {
+          const float x = flag_lds[buf ^ 1][ww];
+          f += x;
+          if (ww / UW == u) fu += x;
+        }
         keep_any = f > 0.f;
-        keep_mine = WV ? (flag_lds[buf ^ 1][w] > 0.f) : keep_any;
+        keep_mine = fu > 0.f;
       }
       if (keep_any) load_tile(vp, jprev, v_lds[buf ^ 1], voff);
-      if (WV) {
-        if (wvis && !keep_mine) ++skipped;
-      } else if (!keep_any) {
-        ++skipped;
-      }
-      keep1 = WV ? (keep_mine && wvis) : keep_any;
+      if (uvis && !keep_mine) ++skipped;
+      // With one unit per workgroup every wave takes the kept tile's
+      // exponentials and P.V (measured faster than letting the waves that
+      // cannot see a diagonal tile drop out); with several units a wave
+      // follows its own unit.
+      keep1 = (UW == NW) ? keep_any : (keep_mine && wvis);
     }
     if (tnext < n_list) load_tile(kp, tile_of(tnext), k_lds[buf ^ 1], koff);
     if (keep2) pv(buf);
@@ -376,29 +387,33 @@ void prefill_kernel(PrefillArgs a) {
     if (have_cur) {
       const int j = tile_of(tcur);
       const uint16_t* kl = k_lds[buf];
-      // S^T = K Q^T for this wave's 32 rows and the tile's 64 keys.
+      // S^T = K Q^T for this wave's 32 rows and the tile's 64 keys; the two
+      // 32-key accumulators alternate so that neither chain waits on itself.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-        const int kr = kb * 32 + r32;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int kr = kb * 32 + r32;
           const int c = (2 * kk + h) ^ swz_k<D>(kr);
-          bf16x8 ka = as_bf16x8(load16(kl + kr * D + c * 8));
+          const bf16x8 ka = as_bf16x8(load16(kl + kr * D + c * 8));
           s[kb] = mfma32(ka, qf[kk], s[kb]);
         }
-      }
       const int kbase = j * BC;
       const bool need_mask = (kbase + BC > L) || (a.causal && kbase + BC - 1 > q0 + w * 32);
       if (need_mask) {
+        // key = kbase + 4h + off(kb, e) with a compile-time off; it is masked
+        // when key > min(row, L - 1) (causal) or key > L - 1. One per-lane
+        // limit instead of a per-element key index keeps registers free.
+        const int lim = (a.causal ? min(row, L - 1) : L - 1) - kbase - 4 * h;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = kbase + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
-            if (key >= L || (a.causal && key > row)) s[kb][e] = -INFINITY;
-          }
+          for (int e = 0; e < 16; ++e)
+            if (kb * 32 + (e >> 2) * 8 + (e & 3) > lim) s[kb][e] = -INFINITY;
       }
       if (NM) nm_sparsify(kbase);
       float mloc = -INFINITY;
@@ -443,38 +458,30 @@ void prefill_kernel(PrefillArgs a) {
       a.lse[(size_t)(b * a.Hq + hq) * L + row] =
           l_tot > 0.f ? m_ref * a.inv_sqrt_d + __logf(l_tot) : -INFINITY;
   }
-  if (a.skip_counts) {
-    if (WV) {
-      if (lane == 0 && wave_rows) a.skip_counts[((size_t)(b * a.Hq + hq) * a.nQ_unit) + i * NW + w] = skipped;
-    } else if (tid == 0) {
-      a.skip_counts[unit] = skipped;
-    }
-  }
+  if (a.skip_counts && lane == 0 && w % UW == 0 && unit_rows) a.skip_counts[unit_id] = skipped;
 }
 
-template <int D, int BR>
+template <int D, int BR, int UW>
 hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)(a.per_xcd * kNumXcd));
   dim3 block(BR * 2);
   const bool stats = a.tile_state || a.tile_margin;
-  const bool sparse = a.block_idx != nullptr;
   const bool nm = a.nm_m > 0 && a.nm_n < a.nm_m;
-  const bool wv = a.wave_vote != 0;
-#define SSA_LAUNCH(ST, SP, NMF, WVF) \
-  hipLaunchKernelGGL((prefill_kernel<D, BR, ST, SP, NMF, WVF>), grid, block, 0, stream, a)
-  if (sparse) {
-    if (stats) SSA_LAUNCH(true, true, false, false);
-    else SSA_LAUNCH(false, true, false, false);
+#define SSA_LAUNCH(ST, SP, NMF) \
+  hipLaunchKernelGGL((prefill_kernel<D, BR, ST, SP, NMF, UW>), grid, block, 0, stream, a)
+  if (a.block_idx != nullptr) {
+    if constexpr (BR / 32 == UW) {
+      if (stats) SSA_LAUNCH(true, true, false);
+      else SSA_LAUNCH(false, true, false);
+    } else {
+      return hipErrorInvalidValue;
+    }
   } else if (nm) {
-    if (stats && wv) SSA_LAUNCH(true, false, true, true);
-    else if (stats) SSA_LAUNCH(true, false, true, false);
-    else if (wv) SSA_LAUNCH(false, false, true, true);
-    else SSA_LAUNCH(false, false, true, false);
+    if (stats) SSA_LAUNCH(true, false, true);
+    else SSA_LAUNCH(false, false, true);
   } else {
-    if (stats && wv) SSA_LAUNCH(true, false, false, true);
-    else if (stats) SSA_LAUNCH(true, false, false, false);
-    else if (wv) SSA_LAUNCH(false, false, false, true);
-    else SSA_LAUNCH(false, false, false, false);
+    if (stats) SSA_LAUNCH(true, false, false);
+    else SSA_LAUNCH(false, false, false);
   }
 #undef SSA_LAUNCH
   return hipGetLastError();
@@ -496,9 +503,10 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.L = p.L;
-  const int br_wg = p.Br == 32 ? 128 : p.Br;  // Br = 32: 128-row workgroups, per-wave votes
+  // Workgroup rows: Br = 32 units run four to a 128-row workgroup (per-wave
+  // votes); Br = 64 and 128 units run one per workgroup.
+  const int br_wg = p.Br == 32 ? 128 : p.Br;
   a.nQ = (p.L + br_wg - 1) / br_wg;
-  a.wave_vote = p.Br == 32 ? 1 : 0;
   a.nQ_unit = (p.L + p.Br - 1) / p.Br;
   a.nK = (p.L + p.Bc - 1) / p.Bc;
   a.G = p.Hq / p.Hkv;
@@ -522,10 +530,16 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   a.nm_m = p.nm_m;
   a.dense_sink = p.dense_sink;
   a.dense_recent = p.dense_recent;
-  if (p.d == 128 && br_wg == 128) return launch<128, 128>(a, stream);
-  if (p.d == 128 && br_wg == 64) return launch<128, 64>(a, stream);
-  if (p.d == 64 && br_wg == 128) return launch<64, 128>(a, stream);
-  if (p.d == 64 && br_wg == 64) return launch<64, 64>(a, stream);
+  if (p.Br == 32) {
+    if (p.d == 128) return launch<128, 128, 1>(a, stream);
+    if (p.d == 64) return launch<64, 128, 1>(a, stream);
+  } else if (p.Br == 128) {
+    if (p.d == 128) return launch<128, 128, 4>(a, stream);
+    if (p.d == 64) return launch<64, 128, 4>(a, stream);
+  } else if (p.Br == 64) {
+    if (p.d == 128) return launch<128, 64, 2>(a, stream);
+    if (p.d == 64) return launch<64, 64, 2>(a, stream);
+  }
   return hipErrorInvalidValue;
 }
 
