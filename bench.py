@@ -409,7 +409,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
-                     "kernel": "prefill_kernel<128,128>", "kernel_ms": round(ev_ms, 4),
+                     "kernel": "prefill_kernel<128, 128, false, false, false, 4>", "kernel_ms": round(ev_ms, 4),
                      "executed_flops": ex},
     }
     del p
