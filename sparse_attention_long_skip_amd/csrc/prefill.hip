@@ -87,7 +87,7 @@ __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 
 // SPARSE: visit a per-tile block list (one unit per workgroup). NM: N:M
 // sparse softmax on the scores before the tile rule.
 template <int D, int BR, bool STATS, bool SPARSE, bool NM, int UW>
-__global__ __launch_bounds__(BR * 2) __attribute__((amdgpu_waves_per_eu(BR >= 256 ? 4 : 2)))
+__global__ __launch_bounds__(BR * 2) __attribute__((amdgpu_waves_per_eu(D == 64 && BR == 64 ? 3 : 2)))
 void prefill_kernel(PrefillArgs a) {
   constexpr int NW = BR / 32;
   constexpr int NU = NW / UW;  // decision units per workgroup
@@ -100,7 +100,12 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int NDB = D / 32;
 
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2][TILE];
+  // d = 64 with 64-row tiles: one V buffer (24 KiB of LDS per workgroup, six
+  // workgroups -- three waves per SIMD -- per CU); the V load of a kept tile
+  // then waits for a second barrier, after every wave's P.V of the tile
+  // before it.
+  constexpr bool VSINGLE = D == 64 && BR == 64;
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[VSINGLE ? 1 : 2][TILE];
   __shared__ float flag_lds[2][NW];
 
   const int tid = threadIdx.x;
@@ -231,7 +236,7 @@ void prefill_kernel(PrefillArgs a) {
   // O^T += V^T P^T from V buffer vb. A operand for (nb, kb, gp): element e
   // of lane (h, r32) = V[kc + 8*(e/4) + 4h + e%4][32 nb + r32].
   auto pv = [&](int vb) {
-    const uint16_t* vt = v_lds[vb];
+    const uint16_t* vt = v_lds[VSINGLE ? 0 : vb];
     const int g16 = lane >> 4;
     const int jj = lane & 15;
 #pragma unroll
@@ -309,6 +314,7 @@ void prefill_kernel(PrefillArgs a) {
     wait_vmem();
     __syncthreads();
     bool keep1 = false;  // this wave takes the exponentials and P.V of tile jprev
+    bool v_due = false;  // some unit keeps tile jprev: its V is loaded
     if (have_prev) {
       // keep_any: some decision unit of the workgroup keeps the tile (V is
       // loaded); keep_mine: this wave's unit keeps it. A unit whose rows
@@ -341,7 +347,8 @@ void prefill_kernel(PrefillArgs a) {
         keep_any = f > 0.f;
         keep_mine = fu > 0.f;
       }
-      if (keep_any) load_tile(vp, jprev, v_lds[buf ^ 1], voff);
+      if (!VSINGLE && keep_any) load_tile(vp, jprev, v_lds[buf ^ 1], voff);
+      v_due = keep_any;
       if (uvis && !keep_mine) ++skipped;
       // With one unit per workgroup every wave takes the kept tile's
       // exponentials and P.V (measured faster than letting the waves that
@@ -351,6 +358,10 @@ void prefill_kernel(PrefillArgs a) {
     }
     if (tnext < n_list) load_tile(kp, tile_of(tnext), k_lds[buf ^ 1], koff);
     if (keep2) pv(buf);
+    if constexpr (VSINGLE) {
+      __syncthreads();  // every wave is done reading V(t-2)
+      if (v_due) load_tile(vp, jprev, v_lds[0], voff);
+    }
     if (keep1) {
       // exp2 with 1/sqrt(d) and log2(e) folded in, against the reference max.
       const bool grow = (m_run > m_ref + tau_raw) || (m_ref == -INFINITY && m_run != -INFINITY);
