@@ -368,7 +368,7 @@ __global__ __launch_bounds__(SEL_T) void vs_select(VsArgs a) {
       o[e] = (by_rank && j < L) ? x[j] : 0.f;
     }
   };
-  float xv[PER], xn[PER];
+  float xv[PER], xn[PER] = {};
   load_step(0, xv);
   uint64_t run = 0;  // (above << 32) | equal, over the keys before this step
   for (int base = 0; base < L; base += STEP) {
