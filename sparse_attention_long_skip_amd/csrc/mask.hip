@@ -22,10 +22,10 @@
 // Kernels: (1) pool -- one workgroup per (block, head, batch, Q-or-K), a
 // single coalesced pass over Q and K (the HBM-bound part), optionally also
 // the block self-similarity ||mean of the unit rows||^2; (2) select -- one
-// workgroup per (4 query blocks, head, batch): scores into LDS as 64-bit
+// workgroup per (4 query blocks, head, batch): scores into LDS as 44-bit
 // keys (order-preserving float bits, then the inverted index so that equal
 // scores put the lower index first); then one wave per row finds the cut by
-// radix selection over the keys, with ballot counts (top-k, Top-tau count)
+// radix selection over the keys below their common prefix, with ballot counts (top-k, Top-tau count)
 // or wave sums of P_hat (Top-tau mass), and compacts the kept set in
 // ascending order.
 #include "common.h"
@@ -182,10 +182,22 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   return x;
 }
 
+// Selection keys: order-preserving score bits above a 12-bit inverted block
+// index (nB <= 4096), so a larger key is a higher score or, on a tie, a
+// lower index. Key 0 is "no candidate".
+constexpr int kIdxBits = 12;
+constexpr uint32_t kIdxMask = (1u << kIdxBits) - 1;
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t x, int o) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, o, kWave);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), o, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // One workgroup per (QPB consecutive query blocks, head, batch). Scores of
-// every causal candidate are turned into 64-bit keys (order-preserving float
-// bits, then the inverted index, so a larger key is a higher score or, on a
-// tie, a lower index). A candidate is in the top-k iff its key is at least
+// every causal candidate are turned into 44-bit keys (order-preserving float
+// bits, then the 12-bit inverted index, so a larger key is a higher score
+// or, on a tie, a lower index). A candidate is in the top-k iff its key is at least
 // the topk-th largest key. The kept set is compacted in ascending order with
 // wave ballots.
 template <int D, int QPB, bool SPARGE, bool COMP>
@@ -243,7 +255,7 @@ __global__ __launch_bounds__(256) void select_kernel(MaskArgs a) {
       if (c <= qb) {
         const float sc = acc[q] * a.inv_sqrt_d;
         if (a.block_scores) a.block_scores[(hb * a.nB + qb) * a.nB + c] = sc;
-        key = ((uint64_t)order_bits(sc) << 32) | (uint64_t)(0xffffffffu - (uint32_t)c);
+        key = ((uint64_t)order_bits(sc) << kIdxBits) | (uint64_t)(kIdxMask - (uint32_t)c);
       }
       keys[q * nBp + c] = key;
     }
@@ -257,8 +269,8 @@ __global__ __launch_bounds__(256) void select_kernel(MaskArgs a) {
   // Selection: wave wv owns row qb0 + wv (QPB == 4 rows per workgroup, or
   // one row handled by wave 0). The top-k threshold is the topk-th largest
   // key T: the largest value with #{key >= T} >= topk (keys are distinct,
-  // so exactly topk keys are >= T), found by a 64-round radix selection
-  // whose counts are wave ballots; no barriers.
+  // so exactly topk keys are >= T), found by a radix descent over the bits
+  // below the row's common key prefix, with wave-ballot counts; no barriers.
   constexpr int NREG = 8;  // rows with at most 512 candidates keep keys in registers
   const int q = (QPB == 1) ? 0 : wv;
   if ((QPB == 1 && wv != 0) || q >= nq) return;
@@ -283,10 +295,36 @@ __global__ __launch_bounds__(256) void select_kernel(MaskArgs a) {
     const int c = r * 64 + lane;
     return c < N ? kq[c] : 0ull;
   };
+  // The live (nonzero) keys share their bits above `top`: the descent starts
+  // from that common prefix. Returns top (-1 when at most one distinct live
+  // key exists, then *thr0 is that key or 0).
+  auto common_prefix = [&](uint64_t* thr0) -> int {
+    uint64_t ka = ~0ull, ko = 0ull;
+    for (int r = 0; r < nch; ++r) {
+      const uint64_t kv = key_at(r);
+      if (kv) {
+        ka &= kv;
+        ko |= kv;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      ka &= shfl_xor64(ka, o);
+      ko |= shfl_xor64(ko, o);
+    }
+    if (ko == 0ull || ka == ko) {
+      *thr0 = ko;
+      return -1;
+    }
+    const int top = 63 - __clzll((long long)(ka ^ ko));
+    *thr0 = top == 63 ? 0ull : (ka & ~((2ull << top) - 1ull));
+    return top;
+  };
   // Largest key T with #{keys >= T} >= need (zero keys never count).
   auto select_by_count = [&](int need) -> uint64_t {
-    uint64_t thr = 0;
-    for (int bit = 63; bit >= 0; --bit) {
+    uint64_t thr;
+    const int top = common_prefix(&thr);
+    for (int bit = top; bit >= 0; --bit) {
       const uint64_t cand = thr | (1ull << bit);
       int cnt = 0;
       if (in_reg) {
@@ -335,7 +373,7 @@ __global__ __launch_bounds__(256) void select_kernel(MaskArgs a) {
           kq[c] = kv;
         }
         ncomp += __popcll(__ballot(comp));
-        hi = max(hi, (uint32_t)(kv >> 32));
+        hi = max(hi, (uint32_t)(kv >> kIdxBits));
       }
       if (ncomp > 0) {
         if (a.tau_mode == 1) {
@@ -347,7 +385,7 @@ __global__ __launch_bounds__(256) void select_kernel(MaskArgs a) {
           float zl = 0.f;
           for (int r = 0; r < nch; ++r) {
             const uint64_t kv = key_at(r);
-            const float p = kv ? fast_exp2((from_order_bits((uint32_t)(kv >> 32)) - smax) * kLog2e) : 0.f;
+            const float p = kv ? fast_exp2((from_order_bits((uint32_t)(kv >> kIdxBits)) - smax) * kLog2e) : 0.f;
             if (in_reg) {
 #pragma unroll
               for (int rr = 0; rr < NREG; ++rr) pr[rr] = (rr == r) ? p : pr[rr];
@@ -360,7 +398,8 @@ __global__ __launch_bounds__(256) void select_kernel(MaskArgs a) {
           // order, so it never grows with T and the radix descent is exact
           // for this predicate. The full set (T = 1) has mass Z >= tau * Z.
           const float target = a.tau * wave_sum(zl);
-          for (int bit = 63; bit >= 0; --bit) {
+          const int top = common_prefix(&thr);
+          for (int bit = top; bit >= 0; --bit) {
             const uint64_t cand = thr | (1ull << bit);
             float m = 0.f;
             if (in_reg) {
