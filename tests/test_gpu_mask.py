@@ -64,3 +64,11 @@ def test_compressed_mask_long_sequence():
     x = synth.prefill_inputs(404, 0, 1, 1, 1, 1100 * 64 - 17, 64)
     r = mask_parity(x["q"], x["k"], 64, 64, 1, 1024, compress=(32, 16))
     print(f"near-tie differences {r['ties']}")
+
+
+def test_masks_batched_heads():
+    # B = 2 for the pooled and the compressed mask
+    x = synth.prefill_inputs(405, 0, 2, 3, 3, 64 * 25 + 33, 64)
+    for compress in (None, (32, 16)):
+        r = mask_parity(x["q"], x["k"], 64, 7, 1, 192, compress=compress)
+        print(f"compress={compress}: near-tie differences {r['ties']}")

@@ -75,3 +75,10 @@ def test_sparge_two_stage_pipeline():
                            block_idx=ref["block_idx"].astype(np.int32),
                            block_cnt=ref["block_cnt"].astype(np.int32))
         print(f"kept blocks {kept:.2f}, lam={lam}: skipped {r['skipped']}/{r['visited']}")
+
+
+def test_sparge_batched_heads():
+    # B = 2: batch and head indexing of every workspace and output
+    x = synth.prefill_inputs(605, 1, 2, 3, 3, 64 * 20 + 9, 64, drift=2.0)
+    r = sparge_parity(x["q"], x["k"], 0.25, 0.8, "mass")
+    print(f"rows at a decision band {r['near']}")

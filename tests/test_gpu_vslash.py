@@ -47,3 +47,11 @@ def test_vslash_pipeline_prefill():
     for lam in (-math.inf, -5.0):
         p = prefill_parity(x["q"], x["k"], x["v"], lam, 64, 64, True, block_idx=bi, block_cnt=bc)
         print(f"lam={lam}: skipped {p['skipped']}/{p['visited']}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_vslash_batched_heads(d):
+    # B = 2: batch and head indexing of every workspace section and output
+    x = synth.prefill_inputs(803, d, 2, 3, 3, 64 * 30 + 7, d)
+    r = vslash_parity(x["q"], x["k"], 48, 90, 20)
+    print(f"heads with near-ties {r['tie_heads']}")
