@@ -58,3 +58,11 @@ def test_workspace_reuse_second_call_smaller():
     torch.cuda.synchronize()
     ref = oracle.decode(y["q"], y["k_cache"], y["v_cache"], [100, 2000], -1.0, 64, 4, bits=True)
     assert np.abs(b["out"].float().cpu().numpy() - ref["out"]).max() < 2e-2
+
+
+@pytest.mark.parametrize("lens", [[1, 63, 64, 65], [127, 128, 129, 2047]])
+def test_length_tile_edges(lens):
+    # cache lengths at and around tile and split boundaries (split of 4 tiles)
+    y = synth.decode_inputs(302, sum(lens), len(lens), 8, 2, 2048, 128, 1, 2048, seqlens=lens)
+    r = decode_parity(y, -0.5, 4)
+    print(f"lens={lens}: skipped {r['skipped']}/{r['visited']}")

@@ -95,3 +95,12 @@ def test_wave_granular_votes(d):
         print(f"d={d} lam={lam:.3f}: skipped {r['skipped']}/{r['visited']} exempt {r['exempt']}")
     r = prefill_parity(q, k, v, -math.inf, 32, 64, False)
     assert r["skipped"] == 0
+
+
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 127, 129, 191])
+@pytest.mark.parametrize("d,Br", [(64, 64), (128, 128), (128, 32)])
+def test_tile_edges(L, d, Br):
+    # lengths at and around tile boundaries, GQA 4/2, a skipping lambda
+    q, k, v = _inputs(202, L, 1, 4, 2, L, d)
+    r = prefill_parity(q, k, v, -0.2, Br, 64, True)
+    print(f"L={L} d={d} Br={Br}: skipped {r['skipped']}/{r['visited']} err {r['max_err_out']:.2e}")
