@@ -91,8 +91,11 @@ __device__ __forceinline__ void load_lds16(const void* gsrc, void* lds_base) {
                                    (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
-// Wait until every global load of this wave (including LDS-direct ones) is done.
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until every global load of this wave (including LDS-direct ones) is
+// done: s_waitcnt with vmcnt = 0 and the other counters at their maximum
+// (expcnt 7, lgkmcnt 15). Issued through the builtin rather than inline asm
+// so that the compiler's own wait insertion knows the loads have landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes,
 // lane li receives element (li % 4) of the 8-byte chunks addressed by lanes

@@ -79,6 +79,11 @@ __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
+template <int N>
+struct StepParity {
+  static constexpr int value = N;
+};
+
 // BR: query rows per workgroup (BR / 32 waves). UW: waves per decision unit
 // (the query tile of Br = 32 * UW rows); a workgroup holds BR / (32 UW)
 // units that vote separately and share the K/V tiles (V is loaded when any
@@ -105,7 +110,13 @@ void prefill_kernel(PrefillArgs a) {
   // then waits for a second barrier, after every wave's P.V of the tile
   // before it.
   constexpr bool VSINGLE = D == 64 && BR == 64;
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[VSINGLE ? 1 : 2][TILE];
+  // The two V buffers are separate LDS objects and every step names its
+  // buffers at compile time (the loop below is unrolled by two): the
+  // compiler then sees that the transposing reads of one V buffer cannot
+  // alias the LDS-direct loads into the other, and does not wait for those
+  // loads to land before the P.V.
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[VSINGLE ? 8 : TILE];
   __shared__ float flag_lds[2][NW];
 
   const int tid = threadIdx.x;
@@ -193,26 +204,30 @@ void prefill_kernel(PrefillArgs a) {
   // Per-lane source offsets are fixed; rows past L (last tile only) read
   // row L-1 (finite data; those scores are masked and their P is 0).
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  int koff[LPW], voff[LPW], lrow[LPW];
+  // Source offsets are in bytes from the tile's first row, as 32-bit
+  // unsigned values (a wave-uniform base plus a 32-bit offset per lane).
+  uint32_t koff[LPW], voff[LPW];
+  int lrow[LPW];
 #pragma unroll
   for (int r = 0; r < LPW; ++r) {
     const int s = (w * LPW + r) * 64 + lane;
     const int rr = s / CPR;
     lrow[r] = rr;
-    koff[r] = rr * D + ((s % CPR) ^ swz_k<D>(rr)) * 8;
-    voff[r] = rr * D + ((s % CPR) ^ swz_v<D>(rr)) * 8;
+    koff[r] = (uint32_t)(rr * D + ((s % CPR) ^ swz_k<D>(rr)) * 8) * 2u;
+    voff[r] = (uint32_t)(rr * D + ((s % CPR) ^ swz_v<D>(rr)) * 8) * 2u;
   }
-  auto load_tile = [&](const uint16_t* src, int j, uint16_t* dst, const int* off) {
+  auto load_tile = [&](const uint16_t* src, int j, uint16_t* dst, const uint32_t* off) __attribute__((always_inline)) {
     const int kb0 = j * BC;
-    const uint16_t* base = src + (size_t)kb0 * D;
+    const char* base = reinterpret_cast<const char*>(src + (size_t)kb0 * D);
     if (kb0 + BC <= L) {
 #pragma unroll
       for (int r = 0; r < LPW; ++r) load_lds16(base + off[r], dst + (wu * LPW + r) * 512);
     } else {
 #pragma unroll
       for (int r = 0; r < LPW; ++r) {
-        const int over = max(kb0 + lrow[r] - (L - 1), 0);
-        load_lds16(base + off[r] - (size_t)over * D, dst + (wu * LPW + r) * 512);
+        // over <= lrow[r], so the offset stays non-negative
+        const uint32_t over = (uint32_t)max(kb0 + lrow[r] - (L - 1), 0);
+        load_lds16(base + (off[r] - over * (uint32_t)(2 * D)), dst + (wu * LPW + r) * 512);
       }
     }
   };
@@ -233,12 +248,26 @@ void prefill_kernel(PrefillArgs a) {
   bool keep2 = false;
   int skipped = 0;
 
-  // O^T += V^T P^T from V buffer vb. A operand for (nb, kb, gp): element e
-  // of lane (h, r32) = V[kc + 8*(e/4) + 4h + e%4][32 nb + r32].
-  auto pv = [&](int vb) {
-    const uint16_t* vt = v_lds[VSINGLE ? 0 : vb];
+  // Per-lane element offsets of the transposing V reads of rows 0..15, one
+  // per 32-column block; rows kc + 0..15 (kc a multiple of 8) add kc * D,
+  // since the V swizzle depends only on row bits that kc leaves unchanged.
+  // The empty asm keeps each offset opaque, so every read address is one
+  // offset from the buffer: the compiler then keeps the alias information
+  // that tells it the read cannot touch the buffer being loaded.
+  int vrd[NDB];
+#pragma unroll
+  for (int nb = 0; nb < NDB; ++nb) {
     const int g16 = lane >> 4;
     const int jj = lane & 15;
+    const int c = nb * 4 + (g16 & 1) * 2 + ((jj & 3) >> 1);
+    const int ra = 4 * h + (jj >> 2);
+    vrd[nb] = ra * D + ((c ^ swz_v<D>(ra)) * 8) + (jj & 1) * 4;
+    asm("" : "+v"(vrd[nb]));
+  }
+
+  // O^T += V^T P^T from the V tile at vt. A operand for (nb, kb, gp): element
+  // e of lane (h, r32) = V[kc + 8*(e/4) + 4h + e%4][32 nb + r32].
+  auto pv = [&](const uint16_t* vt) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -246,11 +275,8 @@ void prefill_kernel(PrefillArgs a) {
         const int kc = kb * 32 + gp * 16;
 #pragma unroll
         for (int nb = 0; nb < NDB; ++nb) {
-          const int c = nb * 4 + (g16 & 1) * 2 + ((jj & 3) >> 1);
-          const int ra = kc + 4 * h + (jj >> 2);
-          const int rb = ra + 8;
-          const uint64_t lo = lds_read_tr16(vt + ra * D + ((c ^ swz_v<D>(ra)) * 8) + (jj & 1) * 4);
-          const uint64_t hi = lds_read_tr16(vt + rb * D + ((c ^ swz_v<D>(rb)) * 8) + (jj & 1) * 4);
+          const uint64_t lo = lds_read_tr16(vt + vrd[nb] + kc * D);
+          const uint64_t hi = lds_read_tr16(vt + vrd[nb] + (kc + 8) * D);
           u32x4 va = {(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
           o[nb] = mfma32(as_bf16x8(va), p[kb * 2 + gp], o[nb]);
         }
@@ -266,7 +292,7 @@ void prefill_kernel(PrefillArgs a) {
   // and keys in (row - dense_recent, row]; the rest become -inf. A lane
   // holds, per 8-key block, 4 consecutive keys (8q + 4h + 0..3), so groups
   // of 2 or 4 are lane-local.
-  auto nm_sparsify = [&](int kbase) {
+  auto nm_sparsify = [&](int kbase) __attribute__((always_inline)) {
     const bool exempt_here = (kbase < a.dense_sink) ||
         (a.dense_recent > 0 && kbase + BC - 1 > q0 + w * 32 - a.dense_recent);
 #pragma unroll
@@ -305,12 +331,14 @@ void prefill_kernel(PrefillArgs a) {
   if (tcur < n_list) load_tile(kp, tile_of(tcur), k_lds[0], koff);
   int tnext = tcur < n_list ? next_valid(tcur + 1) : n_list;
   int jprev = -1;  // tile of the previous position
-  int it = 0;
-  for (;; ++it) {
+  // One pipeline step; BUF = step parity selects the LDS buffers.
+  auto step = [&](auto buf_c) __attribute__((always_inline)) -> bool {
+    constexpr int buf = decltype(buf_c)::value;
+    uint16_t* const v_cur = (buf == 0 || VSINGLE) ? v_lds0 : v_lds1;  // V(t-2), read by P.V
+    uint16_t* const v_nxt = (buf == 1 || VSINGLE) ? v_lds0 : v_lds1;  // V(t-1), loaded now
     const bool have_cur = tcur < n_list;
     const bool have_prev = jprev >= 0;
-    if (!have_cur && !have_prev && !keep2) break;
-    const int buf = it & 1;
+    if (!have_cur && !have_prev && !keep2) return false;
     wait_vmem();
     __syncthreads();
     bool keep1 = false;  // this wave takes the exponentials and P.V of tile jprev
@@ -347,7 +375,7 @@ void prefill_kernel(PrefillArgs a) {
         keep_any = f > 0.f;
         keep_mine = fu > 0.f;
       }
-      if (!VSINGLE && keep_any) load_tile(vp, jprev, v_lds[buf ^ 1], voff);
+      if (!VSINGLE && keep_any) load_tile(vp, jprev, v_nxt, voff);
       v_due = keep_any;
       if (uvis && !keep_mine) ++skipped;
       // With one unit per workgroup every wave takes the kept tile's
@@ -357,10 +385,10 @@ void prefill_kernel(PrefillArgs a) {
       keep1 = (UW == NW) ? keep_any : (keep_mine && wvis);
     }
     if (tnext < n_list) load_tile(kp, tile_of(tnext), k_lds[buf ^ 1], koff);
-    if (keep2) pv(buf);
+    if (keep2) pv(v_cur);
     if constexpr (VSINGLE) {
       __syncthreads();  // every wave is done reading V(t-2)
-      if (v_due) load_tile(vp, jprev, v_lds[0], voff);
+      if (v_due) load_tile(vp, jprev, v_nxt, voff);
     }
     if (keep1) {
       // exp2 with 1/sqrt(d) and log2(e) folded in, against the reference max.
@@ -449,6 +477,9 @@ void prefill_kernel(PrefillArgs a) {
       tcur = tnext;
       tnext = tcur < n_list ? next_valid(tcur + 1) : n_list;
     }
+    return true;
+  };
+  while (step(StepParity<0>{}) && step(StepParity<1>{})) {
   }
 
   // Epilogue: normalise, write out (bf16) and lse.
