@@ -104,17 +104,18 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int NKK = D / 16;
   constexpr int NDB = D / 32;
 
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE];
   // d = 64 with 64-row tiles: one V buffer (24 KiB of LDS per workgroup, six
   // workgroups -- three waves per SIMD -- per CU); the V load of a kept tile
   // then waits for a second barrier, after every wave's P.V of the tile
   // before it.
   constexpr bool VSINGLE = D == 64 && BR == 64;
-  // The two V buffers are separate LDS objects and every step names its
+  // The K and V buffers are separate LDS objects and every step names its
   // buffers at compile time (the loop below is unrolled by two): the
-  // compiler then sees that the transposing reads of one V buffer cannot
-  // alias the LDS-direct loads into the other, and does not wait for those
-  // loads to land before the P.V.
+  // compiler then sees that the reads of one buffer cannot alias the
+  // LDS-direct loads into another, and does not wait for those loads to
+  // land before the P.V or the scores.
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[VSINGLE ? 8 : TILE];
   __shared__ float flag_lds[2][NW];
@@ -189,13 +190,31 @@ void prefill_kernel(PrefillArgs a) {
   } else {
     n_list = a.causal ? (last_row / BC + 1) : a.nK;
   }
-  auto tile_of = [&](int t) -> int { return SPARSE ? list[t] : t; };
+  // A block list is read 64 entries at a time, one per lane, and entry t is
+  // taken from lane t % 64: one vector load per 64 tiles instead of a load
+  // (and a wait behind the tile loads in flight) per tile.
+  int lst_base = -64, lst_val = 0;
+  auto list_at = [&](int t) -> int {
+    const int blk = t & ~63;
+    if (blk != lst_base) {
+      lst_base = blk;
+      lst_val = blk + lane < n_list ? list[blk + lane] : -1;
+    }
+    return __builtin_amdgcn_readlane(lst_val, t & 63);
+  };
   auto valid = [&](int j) -> bool {
     return j >= 0 && j < a.nK && (!a.causal || j * BC <= last_row);
   };
-  auto next_valid = [&](int t) -> int {
-    if (!SPARSE) return t;
-    while (t < n_list && !valid(list[t])) ++t;
+  // First valid list position >= t (n_list if none) and its tile j.
+  auto advance = [&](int t, int& j) -> int {
+    if (!SPARSE) {
+      j = t;
+      return t;
+    }
+    for (; t < n_list; ++t) {
+      j = list_at(t);
+      if (valid(j)) break;
+    }
     return t;
   };
 
@@ -265,6 +284,16 @@ void prefill_kernel(PrefillArgs a) {
     asm("" : "+v"(vrd[nb]));
   }
 
+  // Per-lane element offsets of the K row reads for the scores, one per
+  // 16-wide reduction slice kk (key row r32; rows 32 + r32 add 32 * D, the K
+  // swizzle depending only on the low row bits), opaque for the same reason.
+  int krd[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    krd[kk] = r32 * D + (((2 * kk + h) ^ swz_k<D>(r32)) * 8);
+    asm("" : "+v"(krd[kk]));
+  }
+
   // O^T += V^T P^T from the V tile at vt. A operand for (nb, kb, gp): element
   // e of lane (h, r32) = V[kc + 8*(e/4) + 4h + e%4][32 nb + r32].
   auto pv = [&](const uint16_t* vt) __attribute__((always_inline)) {
@@ -327,15 +356,18 @@ void prefill_kernel(PrefillArgs a) {
       }
   };
 
-  int tcur = next_valid(0);
-  if (tcur < n_list) load_tile(kp, tile_of(tcur), k_lds[0], koff);
-  int tnext = tcur < n_list ? next_valid(tcur + 1) : n_list;
+  int jcur = 0, jnext = 0;  // tiles at list positions tcur and tnext
+  int tcur = advance(0, jcur);
+  if (tcur < n_list) load_tile(kp, jcur, k_lds0, koff);
+  int tnext = tcur < n_list ? advance(tcur + 1, jnext) : n_list;
   int jprev = -1;  // tile of the previous position
   // One pipeline step; BUF = step parity selects the LDS buffers.
   auto step = [&](auto buf_c) __attribute__((always_inline)) -> bool {
     constexpr int buf = decltype(buf_c)::value;
     uint16_t* const v_cur = (buf == 0 || VSINGLE) ? v_lds0 : v_lds1;  // V(t-2), read by P.V
     uint16_t* const v_nxt = (buf == 1 || VSINGLE) ? v_lds0 : v_lds1;  // V(t-1), loaded now
+    uint16_t* const k_cur = buf == 0 ? k_lds0 : k_lds1;  // K(t), read by the scores
+    uint16_t* const k_nxt = buf == 0 ? k_lds1 : k_lds0;  // K(t+1), loaded now
     const bool have_cur = tcur < n_list;
     const bool have_prev = jprev >= 0;
     if (!have_cur && !have_prev && !keep2) return false;
@@ -384,10 +416,17 @@ void prefill_kernel(PrefillArgs a) {
       // follows its own unit.
       keep1 = (UW == NW) ? keep_any : (keep_mine && wvis);
     }
-    if (tnext < n_list) load_tile(kp, tile_of(tnext), k_lds[buf ^ 1], koff);
+    if (tnext < n_list) load_tile(kp, jnext, k_nxt, koff);
     if (keep2) pv(v_cur);
     if constexpr (VSINGLE) {
-      __syncthreads();  // every wave is done reading V(t-2)
+      // Every wave is done reading V(t-2) before any wave loads V(t-1) into
+      // the same buffer: this wave's LDS reads have returned (lgkmcnt 0;
+      // vmcnt and expcnt left at their maximum), then a plain barrier. A
+      // full __syncthreads() would also wait for the K(t+1) loads in flight.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
       if (v_due) load_tile(vp, jprev, v_nxt, voff);
     }
     if (keep1) {
@@ -424,8 +463,8 @@ void prefill_kernel(PrefillArgs a) {
     keep2 = keep1;
     jprev = -1;
     if (have_cur) {
-      const int j = tile_of(tcur);
-      const uint16_t* kl = k_lds[buf];
+      const int j = jcur;
+      const uint16_t* kl = k_cur;
       // S^T = K Q^T for this wave's 32 rows and the tile's 64 keys; the two
       // 32-key accumulators alternate so that neither chain waits on itself.
 #pragma unroll
@@ -436,9 +475,7 @@ void prefill_kernel(PrefillArgs a) {
       for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const int kr = kb * 32 + r32;
-          const int c = (2 * kk + h) ^ swz_k<D>(kr);
-          const bf16x8 ka = as_bf16x8(load16(kl + kr * D + c * 8));
+          const bf16x8 ka = as_bf16x8(load16(kl + krd[kk] + kb * 32 * D));
           s[kb] = mfma32(ka, qf[kk], s[kb]);
         }
       const int kbase = j * BC;
@@ -475,7 +512,8 @@ void prefill_kernel(PrefillArgs a) {
       m_run = fmaxf(m_run, mloc);
       jprev = j;
       tcur = tnext;
-      tnext = tcur < n_list ? next_valid(tcur + 1) : n_list;
+      jcur = jnext;
+      tnext = tcur < n_list ? advance(tcur + 1, jnext) : n_list;
     }
     return true;
   };
