@@ -10,8 +10,10 @@
 //    waves, each owning 32 query rows; two workgroups per CU so that one
 //    workgroup's exponentials overlap the other's matrix work. The decision
 //    unit is the whole query tile, or, with Br = 32, each wave (SpargeAttn's
-//    warp-granular variant): then a wave skips its own exponentials and P.V,
-//    and the shared V tile is loaded when any wave keeps it.
+//    warp-granular variant). A tile that some unit keeps is loaded and run
+//    through every wave of the workgroup; in a wave whose unit skips it the
+//    exponentials are forced to zero, so the result is that of the per-unit
+//    rule.
 //  * Scores are computed transposed, S^T = K Q^T, with 32x32x16 bf16 MFMA:
 //    K rows come from LDS (A operand), Q stays in registers (B operand). The
 //    accumulator then gives every lane ONE query row (lane % 32) and 16 keys
@@ -24,15 +26,16 @@
 //  * K and V tiles go from HBM to LDS with LDS-direct 16-byte loads (no
 //    staging registers), into XOR-swizzled rows so that both the K row reads
 //    and the transposing V reads are free of bank conflicts. K and V are
-//    double-buffered.
+//    double-buffered (V alternates per kept tile).
 //  * Software pipeline over the visited tiles, ONE barrier per step t:
-//      wait for this wave's loads; barrier (K(t), V(t-2), flags(t-1) visible);
-//      workgroup vote of tile t-1 (OR of the per-wave ballots); if kept,
-//      issue the V(t-1) loads; issue the K(t+1) loads; P.V of tile t-2
-//      (MFMA); if tile t-1 is kept, exp -> P(t-1) (bf16 registers); scores of
-//      tile t (MFMA), row max, gap against the running max, wave ballot.
-//    So V is fetched only for kept tiles and has a whole step to land, and
-//    the exponentials of one tile sit between two blocks of matrix work.
+//      wait for this wave's loads; barrier (K(t), the last kept V, flags(t-1)
+//      visible); workgroup vote of tile t-1 (OR of the per-wave ballots);
+//      issue the K(t+1) loads; if tile t-1 is kept: P.V of the previous kept
+//      tile interleaved with exp -> P(t-1) (bf16 registers), chunk by chunk,
+//      then the V(t-1) loads; scores of tile t (MFMA), row max, gap against
+//      the running max, wave ballot.
+//    So V is fetched only for kept tiles and has at least a whole step to
+//    land, and the exponentials run in the shadow of the matrix work.
 //  * The exponentials use a reference max that lags the running max: O and
 //    the row sum are rescaled only when a row max exceeds the reference by
 //    more than 2^8 in the exp2 domain (softmax is exact for any reference;
@@ -111,13 +114,13 @@ void prefill_kernel(PrefillArgs a) {
   // then waits for a second barrier, after every wave's P.V of the tile
   // before it.
   constexpr bool VSINGLE = D == 64 && BR == 64;
-  // The K and V buffers are separate LDS objects and every step names its
-  // buffers at compile time (the loop below is unrolled by two): the
-  // compiler then sees that the reads of one buffer cannot alias the
-  // LDS-direct loads into another, and does not wait for those loads to
-  // land before the P.V or the scores.
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[VSINGLE ? 8 : TILE];
+  // The two K buffers are separate LDS objects and every step names its K
+  // buffers at compile time (the loop below is unrolled by two); the V
+  // buffers alternate per kept tile. The compiler then sees that the reads
+  // of one buffer cannot alias the LDS-direct loads into another (V is
+  // loaded after the P.V reads of a step), and does not wait for loads in
+  // flight before the P.V or the scores.
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[VSINGLE ? 1 : 2][TILE];
   __shared__ float flag_lds[2][NW];
 
   const int tid = threadIdx.x;
@@ -157,11 +160,7 @@ void prefill_kernel(PrefillArgs a) {
   const int row = q0 + w * 32 + r32;
   const bool row_ok = row < L;
   const int last_row = min(q0 + BR, L) - 1;
-  // This wave's rows: a tile none of them can see contributes nothing to
-  // them, so the wave skips its exponentials and P.V there. Its decision
-  // unit u covers rows [q0 + 32 UW u, q0 + 32 UW (u + 1)).
-  const bool wave_rows = q0 + w * 32 < L;
-  const int wave_last = min(q0 + w * 32 + 31, L - 1);
+  // This wave's decision unit u covers rows [q0 + 32 UW u, q0 + 32 UW (u + 1)).
   const int u = w / UW;
   const bool unit_rows = q0 + u * UW * 32 < L;
   const int unit_last = min(q0 + (u + 1) * UW * 32 - 1, L - 1);
@@ -235,19 +234,16 @@ void prefill_kernel(PrefillArgs a) {
     koff[r] = (uint32_t)(rr * D + ((s % CPR) ^ swz_k<D>(rr)) * 8) * 2u;
     voff[r] = (uint32_t)(rr * D + ((s % CPR) ^ swz_v<D>(rr)) * 8) * 2u;
   }
+  // No branch for the ragged last tile (the clamp costs three integer ops
+  // per load), so that a load does not split the block it sits in.
   auto load_tile = [&](const uint16_t* src, int j, uint16_t* dst, const uint32_t* off) __attribute__((always_inline)) {
     const int kb0 = j * BC;
     const char* base = reinterpret_cast<const char*>(src + (size_t)kb0 * D);
-    if (kb0 + BC <= L) {
 #pragma unroll
-      for (int r = 0; r < LPW; ++r) load_lds16(base + off[r], dst + (wu * LPW + r) * 512);
-    } else {
-#pragma unroll
-      for (int r = 0; r < LPW; ++r) {
-        // over <= lrow[r], so the offset stays non-negative
-        const uint32_t over = (uint32_t)max(kb0 + lrow[r] - (L - 1), 0);
-        load_lds16(base + (off[r] - over * (uint32_t)(2 * D)), dst + (wu * LPW + r) * 512);
-      }
+    for (int r = 0; r < LPW; ++r) {
+      // over <= lrow[r], so the offset stays non-negative
+      const uint32_t over = (uint32_t)max(kb0 + lrow[r] - (L - 1), 0);
+      load_lds16(base + (off[r] - over * (uint32_t)(2 * D)), dst + (wu * LPW + r) * 512);
     }
   };
 
@@ -263,8 +259,14 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[nb][e] = 0.f;
   f32x16 s[2];  // scores of the latest tile
-  bf16x8 p[4];  // P of the kept tile awaiting its P.V
-  bool keep2 = false;
+  // P of the last kept tile, awaiting its P.V (V in buffer vpar). Before
+  // the first kept tile it is zero against a zeroed V buffer.
+  bf16x8 p[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) p[c] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  int vpar = 0;
+#pragma unroll
+  for (int x = tid; x < TILE / 8; x += NT) store16(v_lds[0] + x * 8, u32x4{0u, 0u, 0u, 0u});
   int skipped = 0;
 
   // Per-lane element offsets of the transposing V reads of rows 0..15, one
@@ -296,20 +298,31 @@ void prefill_kernel(PrefillArgs a) {
 
   // O^T += V^T P^T from the V tile at vt. A operand for (nb, kb, gp): element
   // e of lane (h, r32) = V[kc + 8*(e/4) + 4h + e%4][32 nb + r32].
-  auto pv = [&](const uint16_t* vt) __attribute__((always_inline)) {
+  // P chunk c (keys 16c .. 16c + 15 of a tile) is p[c]; it comes from the
+  // scores s[c / 2][8 (c % 2) .. 8 (c % 2) + 7].
+  auto pv_chunk = [&](const uint16_t* vt, int c) __attribute__((always_inline)) {
+    const int kc = c * 16;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int nb = 0; nb < NDB; ++nb) {
+      const uint64_t lo = lds_read_tr16(vt + vrd[nb] + kc * D);
+      const uint64_t hi = lds_read_tr16(vt + vrd[nb] + (kc + 8) * D);
+      u32x4 va = {(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+      o[nb] = mfma32(as_bf16x8(va), p[c], o[nb]);
+    }
+  };
+  // exp2 of chunk c of the latest scores, with 1/sqrt(d) and log2(e) folded
+  // in, against the scaled reference mc; packed to bf16 into p[c].
+  auto exp_chunk = [&](int c, float mc, float& psum) __attribute__((always_inline)) {
+    const int kb = c >> 1, gp = c & 1;
+    u32x4 pk;
 #pragma unroll
-      for (int gp = 0; gp < 2; ++gp) {
-        const int kc = kb * 32 + gp * 16;
-#pragma unroll
-        for (int nb = 0; nb < NDB; ++nb) {
-          const uint64_t lo = lds_read_tr16(vt + vrd[nb] + kc * D);
-          const uint64_t hi = lds_read_tr16(vt + vrd[nb] + (kc + 8) * D);
-          u32x4 va = {(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
-          o[nb] = mfma32(as_bf16x8(va), p[kb * 2 + gp], o[nb]);
-        }
-      }
+    for (int e = 0; e < 8; e += 2) {
+      const float x0 = fast_exp2(fmaf(s[kb][gp * 8 + e], a.c_log2, -mc));
+      const float x1 = fast_exp2(fmaf(s[kb][gp * 8 + e + 1], a.c_log2, -mc));
+      psum += x0 + x1;
+      pk[e >> 1] = cvt_pk_bf16(x0, x1);
+    }
+    p[c] = as_bf16x8(pk);
   };
 
   // Pipeline over list positions t = 0 .. n+1, one barrier each:
@@ -364,23 +377,19 @@ void prefill_kernel(PrefillArgs a) {
   // One pipeline step; BUF = step parity selects the LDS buffers.
   auto step = [&](auto buf_c) __attribute__((always_inline)) -> bool {
     constexpr int buf = decltype(buf_c)::value;
-    uint16_t* const v_cur = (buf == 0 || VSINGLE) ? v_lds0 : v_lds1;  // V(t-2), read by P.V
-    uint16_t* const v_nxt = (buf == 1 || VSINGLE) ? v_lds0 : v_lds1;  // V(t-1), loaded now
     uint16_t* const k_cur = buf == 0 ? k_lds0 : k_lds1;  // K(t), read by the scores
     uint16_t* const k_nxt = buf == 0 ? k_lds1 : k_lds0;  // K(t+1), loaded now
     const bool have_cur = tcur < n_list;
     const bool have_prev = jprev >= 0;
-    if (!have_cur && !have_prev && !keep2) return false;
+    if (!have_cur && !have_prev) return false;
     wait_vmem();
     __syncthreads();
-    bool keep1 = false;  // this wave takes the exponentials and P.V of tile jprev
-    bool v_due = false;  // some unit keeps tile jprev: its V is loaded
+    bool keep1 = false;     // some unit keeps tile jprev: exponentials, P.V, V load
+    bool keep_mine = false;  // this wave's unit keeps it
     if (have_prev) {
-      // keep_any: some decision unit of the workgroup keeps the tile (V is
-      // loaded); keep_mine: this wave's unit keeps it. A unit whose rows
-      // cannot see the tile (causal) does not count it as visited.
-      bool keep_any, keep_mine;
-      const bool wvis = wave_rows && (!a.causal || jprev * BC <= wave_last);
+      // keep1: some decision unit of the workgroup keeps the tile;
+      // keep_mine: this wave's unit keeps it. A unit whose rows cannot see
+      // the tile (causal) does not count it as visited.
       const bool uvis = unit_rows && (!a.causal || jprev * BC <= unit_last);
       if (STATS) {
         float gu = flag_lds[buf ^ 1][u * UW];
@@ -389,7 +398,7 @@ void prefill_kernel(PrefillArgs a) {
         float g = gu;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) g = fmaxf(g, flag_lds[buf ^ 1][ww]);
-        keep_any = !(g < a.lam_raw);
+        keep1 = !(g < a.lam_raw);
         keep_mine = !(gu < a.lam_raw);
         if (lane == 0 && w % UW == 0 && uvis) {
           const size_t ti = unit_id * a.nK + jprev;
@@ -404,63 +413,68 @@ void prefill_kernel(PrefillArgs a) {
           f += x;
           if (ww / UW == u) fu += x;
         }
-        keep_any = f > 0.f;
+        keep1 = f > 0.f;
         keep_mine = fu > 0.f;
       }
-      if (!VSINGLE && keep_any) load_tile(vp, jprev, v_nxt, voff);
-      v_due = keep_any;
       if (uvis && !keep_mine) ++skipped;
-      // With one unit per workgroup every wave takes the kept tile's
-      // exponentials and P.V (measured faster than letting the waves that
-      // cannot see a diagonal tile drop out); with several units a wave
-      // follows its own unit.
-      keep1 = (UW == NW) ? keep_any : (keep_mine && wvis);
     }
     if (tnext < n_list) load_tile(kp, jnext, k_nxt, koff);
-    if (keep2) pv(v_cur);
-    if constexpr (VSINGLE) {
-      // Every wave is done reading V(t-2) before any wave loads V(t-1) into
-      // the same buffer: this wave's LDS reads have returned (lgkmcnt 0;
-      // vmcnt and expcnt left at their maximum), then a plain barrier. A
-      // full __syncthreads() would also wait for the K(t+1) loads in flight.
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (v_due) load_tile(vp, jprev, v_nxt, voff);
-    }
     if (keep1) {
-      // exp2 with 1/sqrt(d) and log2(e) folded in, against the reference max.
-      const bool grow = (m_run > m_ref + tau_raw) || (m_ref == -INFINITY && m_run != -INFINITY);
+      // Every wave of the workgroup takes a tile that some unit keeps (the
+      // V tile and the P.V pipeline are shared); in a wave whose unit
+      // skips it the exponentials are exp2(-inf) = 0, so the tile adds
+      // nothing to its rows.
+      // A reference max that grew is taken first: O, the row sum and the
+      // pending P (still to be multiplied into O) move to the new reference.
+      // Then the P.V of the previous kept tile and the exponentials of this
+      // one run in one block: chunk c of the old P feeds the matrix cores
+      // while the exponentials refill chunk c - 1.
+      const bool grow = keep_mine && ((m_run > m_ref + tau_raw) || (m_ref == -INFINITY && m_run != -INFINITY));
       if (__ballot(grow) != 0ull) {
-        const float m_tgt = grow ? m_run : m_ref;
-        const float alpha = (m_ref == -INFINITY) ? 0.f : fast_exp2((m_ref - m_tgt) * a.c_log2);
-        l_acc *= alpha;
+        float alpha = 1.f;
+        if (grow) {
+          alpha = (m_ref == -INFINITY) ? 0.f : fast_exp2((m_ref - m_run) * a.c_log2);
+          m_ref = m_run;
+        }
 #pragma unroll
         for (int nb = 0; nb < NDB; ++nb)
 #pragma unroll
           for (int e = 0; e < 16; ++e) o[nb][e] *= alpha;
-        m_ref = m_tgt;
-      }
-      const float mc = (m_ref == -INFINITY ? 0.f : m_ref) * a.c_log2;
-      float psum = 0.f;
+        l_acc *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int c = 0; c < 4; ++c) {
+          u32x4 w4 = as_u32x4(p[c]);
 #pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-          u32x4 pk;
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float x0 = fast_exp2(fmaf(s[kb][gp * 8 + e], a.c_log2, -mc));
-            const float x1 = fast_exp2(fmaf(s[kb][gp * 8 + e + 1], a.c_log2, -mc));
-            psum += x0 + x1;
-            pk[e >> 1] = cvt_pk_bf16(x0, x1);
-          }
-          p[kb * 2 + gp] = as_bf16x8(pk);
+          for (int x = 0; x < 4; ++x) w4[x] = cvt_pk_bf16(bf16_lo(w4[x]) * alpha, bf16_hi(w4[x]) * alpha);
+          p[c] = as_bf16x8(w4);
         }
+      }
+      const float mc = !keep_mine ? INFINITY : (m_ref == -INFINITY ? 0.f : m_ref * a.c_log2);
+      const uint16_t* vt = v_lds[VSINGLE ? 0 : vpar];
+      float psum = 0.f;
+      pv_chunk(vt, 0);
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {
+        pv_chunk(vt, c + 1);
+        exp_chunk(c, mc, psum);
+      }
+      exp_chunk(3, mc, psum);
       l_acc += psum;
+      if constexpr (VSINGLE) {
+        // Every wave is done reading the V buffer before any wave loads
+        // V(t-1) into it: this wave's LDS reads have returned (lgkmcnt 0;
+        // vmcnt and expcnt left at their maximum), then a plain barrier (a
+        // full __syncthreads() would also wait for the K(t+1) loads).
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        load_tile(vp, jprev, v_lds[0], voff);
+      } else {
+        vpar ^= 1;
+        load_tile(vp, jprev, v_lds[vpar], voff);
+      }
     }
-    keep2 = keep1;
     jprev = -1;
     if (have_cur) {
       const int j = jcur;
@@ -519,6 +533,11 @@ void prefill_kernel(PrefillArgs a) {
   };
   while (step(StepParity<0>{}) && step(StepParity<1>{})) {
   }
+  // P.V of the last kept tile (of zeros if none was kept).
+  wait_vmem();
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < 4; ++c) pv_chunk(v_lds[VSINGLE ? 0 : vpar], c);
 
   // Epilogue: normalise, write out (bf16) and lse.
   const float l_tot = sum_halves(l_acc);
