@@ -86,6 +86,10 @@ template <int N>
 struct StepParity {
   static constexpr int value = N;
 };
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
 
 // BR: query rows per workgroup (BR / 32 waves). UW: waves per decision unit
 // (the query tile of Br = 32 * UW rows); a workgroup holds BR / (32 UW)
@@ -234,16 +238,23 @@ void prefill_kernel(PrefillArgs a) {
     koff[r] = (uint32_t)(rr * D + ((s % CPR) ^ swz_k<D>(rr)) * 8) * 2u;
     voff[r] = (uint32_t)(rr * D + ((s % CPR) ^ swz_v<D>(rr)) * 8) * 2u;
   }
-  // No branch for the ragged last tile (the clamp costs three integer ops
-  // per load), so that a load does not split the block it sits in.
-  auto load_tile = [&](const uint16_t* src, int j, uint16_t* dst, const uint32_t* off) __attribute__((always_inline)) {
+  // With branchy set the ragged last tile takes a separate loop; otherwise
+  // the clamp is applied to every tile (four integer ops per load), and no
+  // branch splits the block the loads sit in.
+  auto load_tile = [&](const uint16_t* src, int j, uint16_t* dst, const uint32_t* off, auto branchy)
+                       __attribute__((always_inline)) {
     const int kb0 = j * BC;
     const char* base = reinterpret_cast<const char*>(src + (size_t)kb0 * D);
+    if (decltype(branchy)::value && kb0 + BC <= L) {
 #pragma unroll
-    for (int r = 0; r < LPW; ++r) {
-      // over <= lrow[r], so the offset stays non-negative
-      const uint32_t over = (uint32_t)max(kb0 + lrow[r] - (L - 1), 0);
-      load_lds16(base + (off[r] - over * (uint32_t)(2 * D)), dst + (wu * LPW + r) * 512);
+      for (int r = 0; r < LPW; ++r) load_lds16(base + off[r], dst + (wu * LPW + r) * 512);
+    } else {
+#pragma unroll
+      for (int r = 0; r < LPW; ++r) {
+        // over <= lrow[r], so the offset stays non-negative
+        const uint32_t over = (uint32_t)max(kb0 + lrow[r] - (L - 1), 0);
+        load_lds16(base + (off[r] - over * (uint32_t)(2 * D)), dst + (wu * LPW + r) * 512);
+      }
     }
   };
 
@@ -310,6 +321,17 @@ void prefill_kernel(PrefillArgs a) {
       o[nb] = mfma32(as_bf16x8(va), p[c], o[nb]);
     }
   };
+  // S^T = K Q^T, keys 32 kb .. 32 kb + 31 of the K tile at kl, for this
+  // wave's 32 rows (one accumulator chain).
+  auto scores_half = [&](const uint16_t* kl, int kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const bf16x8 ka = as_bf16x8(load16(kl + krd[kk] + kb * 32 * D));
+      s[kb] = mfma32(ka, qf[kk], s[kb]);
+    }
+  };
   // exp2 of chunk c of the latest scores, with 1/sqrt(d) and log2(e) folded
   // in, against the scaled reference mc; packed to bf16 into p[c].
   auto exp_chunk = [&](int c, float mc, float& psum) __attribute__((always_inline)) {
@@ -371,7 +393,7 @@ void prefill_kernel(PrefillArgs a) {
 
   int jcur = 0, jnext = 0;  // tiles at list positions tcur and tnext
   int tcur = advance(0, jcur);
-  if (tcur < n_list) load_tile(kp, jcur, k_lds0, koff);
+  if (tcur < n_list) load_tile(kp, jcur, k_lds0, koff, Flag<true>{});
   int tnext = tcur < n_list ? advance(tcur + 1, jnext) : n_list;
   int jprev = -1;  // tile of the previous position
   // One pipeline step; BUF = step parity selects the LDS buffers.
@@ -418,7 +440,7 @@ void prefill_kernel(PrefillArgs a) {
       }
       if (uvis && !keep_mine) ++skipped;
     }
-    if (tnext < n_list) load_tile(kp, jnext, k_nxt, koff);
+    if (tnext < n_list) load_tile(kp, jnext, k_nxt, koff, Flag<true>{});
     if (keep1) {
       // Every wave of the workgroup takes a tile that some unit keeps (the
       // V tile and the P.V pipeline are shared); in a wave whose unit
@@ -458,9 +480,8 @@ void prefill_kernel(PrefillArgs a) {
         pv_chunk(vt, c + 1);
         exp_chunk(c, mc, psum);
       }
-      exp_chunk(3, mc, psum);
-      l_acc += psum;
       if constexpr (VSINGLE) {
+        exp_chunk(3, mc, psum);
         // Every wave is done reading the V buffer before any wave loads
         // V(t-1) into it: this wave's LDS reads have returned (lgkmcnt 0;
         // vmcnt and expcnt left at their maximum), then a plain barrier (a
@@ -469,18 +490,20 @@ void prefill_kernel(PrefillArgs a) {
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        load_tile(vp, jprev, v_lds[0], voff);
+        load_tile(vp, jprev, v_lds[0], voff, Flag<false>{});
       } else {
         vpar ^= 1;
-        load_tile(vp, jprev, v_lds[vpar], voff);
+        load_tile(vp, jprev, v_lds[vpar], voff, Flag<false>{});
+        // The scores of tile t (run even past the last tile, where they are
+        // not used) overlap the last exponential chunk: keys 0..31 go to
+        // s[0], already consumed, while chunk 3 reads s[1].
+        scores_half(k_cur, 0);
+        exp_chunk(3, mc, psum);
+        scores_half(k_cur, 1);
       }
+      l_acc += psum;
     }
-    jprev = -1;
-    if (have_cur) {
-      const int j = jcur;
-      const uint16_t* kl = k_cur;
-      // S^T = K Q^T for this wave's 32 rows and the tile's 64 keys; the two
-      // 32-key accumulators alternate so that neither chain waits on itself.
+    if (have_cur && (VSINGLE || !keep1)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -489,9 +512,13 @@ void prefill_kernel(PrefillArgs a) {
       for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 ka = as_bf16x8(load16(kl + krd[kk] + kb * 32 * D));
+          const bf16x8 ka = as_bf16x8(load16(k_cur + krd[kk] + kb * 32 * D));
           s[kb] = mfma32(ka, qf[kk], s[kb]);
         }
+    }
+    jprev = -1;
+    if (have_cur) {
+      const int j = jcur;
       const int kbase = j * BC;
       const bool need_mask = (kbase + BC > L) || (a.causal && kbase + BC - 1 > q0 + w * 32);
       if (need_mask) {
