@@ -29,11 +29,11 @@
 //    double-buffered (V alternates per kept tile).
 //  * Software pipeline over the visited tiles, ONE barrier per step t:
 //      wait for this wave's loads; barrier (K(t), the last kept V, flags(t-1)
-//      visible); workgroup vote of tile t-1 (OR of the per-wave ballots);
-//      issue the K(t+1) loads; if tile t-1 is kept: P.V of the previous kept
-//      tile interleaved with exp -> P(t-1) (bf16 registers), chunk by chunk,
-//      then the V(t-1) loads; scores of tile t (MFMA), row max, gap against
-//      the running max, wave ballot.
+//      visible); workgroup vote of tile t-1 (OR of the per-wave ballots); if
+//      tile t-1 is kept: P.V of the previous kept tile interleaved with
+//      exp -> P(t-1) (bf16 registers), chunk by chunk, then the V(t-1)
+//      loads; scores of tile t (MFMA); the K(t+1) loads; row max, gap
+//      against the running max, wave ballot.
 //    So V is fetched only for kept tiles and has at least a whole step to
 //    land, and the exponentials run in the shadow of the matrix work.
 //  * The exponentials use a reference max that lags the running max: O and
@@ -440,7 +440,6 @@ void prefill_kernel(PrefillArgs a) {
       }
       if (uvis && !keep_mine) ++skipped;
     }
-    if (tnext < n_list) load_tile(kp, jnext, k_nxt, koff, Flag<true>{});
     if (keep1) {
       // Every wave of the workgroup takes a tile that some unit keeps (the
       // V tile and the P.V pipeline are shared); in a wave whose unit
@@ -516,6 +515,10 @@ void prefill_kernel(PrefillArgs a) {
           s[kb] = mfma32(ka, qf[kk], s[kb]);
         }
     }
+    // K(t+1) is issued after the scores of tile t: the loads queue behind
+    // the other waves' loads while the matrix cores work (measured ~1%
+    // faster than issuing them right after the vote).
+    if (tnext < n_list) load_tile(kp, jnext, k_nxt, koff, Flag<true>{});
     jprev = -1;
     if (have_cur) {
       const int j = jcur;
