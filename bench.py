@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -35,13 +36,19 @@ def log(msg):
 
 
 def kernel_source_hash(files=("common.h", "launch.h", "prefill.hip")) -> str:
-    """Hash of the sources the prefill kernel is built from (the counters in
-    profiles/ are valid only for this exact kernel)."""
+    """Hash of the code the prefill kernel is built from (the counters in
+    profiles/ are valid only for this exact kernel). Comments and runs of
+    white space are dropped first, so an edit that cannot change the
+    compiled kernel keeps the hash."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_attention_long_skip_amd", "csrc")
     for f in files:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        text = " ".join(text.split())
+        h.update(f.encode() + text.encode())
     return h.hexdigest()[:16]
 
 

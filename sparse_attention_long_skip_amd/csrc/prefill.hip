@@ -347,9 +347,6 @@ void prefill_kernel(PrefillArgs a) {
     p[c] = as_bf16x8(pk);
   };
 
-  // Pipeline over list positions t = 0 .. n+1, one barrier each:
-  //   vote of tile t-1 -> issue V(t-1); issue K(t+1); P.V of tile t-2;
-  //   exp of tile t-1; scores, row max and wave flag of tile t.
   // N:M sparse softmax (Model Optimizer tutorial, step 2; FAQ on sink and
   // recent tokens): in every aligned group of M consecutive keys a row keeps
   // its top-N allowed scores (ties: lower key), plus keys below dense_sink
@@ -396,7 +393,10 @@ void prefill_kernel(PrefillArgs a) {
   if (tcur < n_list) load_tile(kp, jcur, k_lds0, koff, Flag<true>{});
   int tnext = tcur < n_list ? advance(tcur + 1, jnext) : n_list;
   int jprev = -1;  // tile of the previous position
-  // One pipeline step; BUF = step parity selects the LDS buffers.
+  // One pipeline step per list position t (the loop runs t = 0 .. n, one
+  // barrier each): vote of tile t-1; if kept, P.V of the previous kept tile
+  // with the exponentials of tile t-1, then V(t-1); scores of tile t; K(t+1);
+  // row max and wave flag of tile t. buf = step parity selects the K buffers.
   auto step = [&](auto buf_c) __attribute__((always_inline)) -> bool {
     constexpr int buf = decltype(buf_c)::value;
     uint16_t* const k_cur = buf == 0 ? k_lds0 : k_lds1;  // K(t), read by the scores
