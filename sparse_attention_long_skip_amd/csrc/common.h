@@ -91,6 +91,21 @@ __device__ __forceinline__ void load_lds16(const void* gsrc, void* lds_base) {
                                    (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
+// Buffer resource over [base, base + nbytes): loads through it return zero
+// (and an LDS-direct load writes zero) for every dword at or past nbytes.
+// The last dword holds the gfx9 buffer format word.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
+}
+
+// Asynchronous 16-byte buffer -> LDS copy: lane i's chunk at byte offset
+// voff of the buffer lands at lds_base + 16 * i (lds_base wave-uniform);
+// out-of-range chunks land as zeros.
+__device__ __forceinline__ void load_lds16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_base, 16, (int)voff, 0,
+                                           0, 0);
+}
+
 // Wait until every global load of this wave (including LDS-direct ones) is
 // done: s_waitcnt with vmcnt = 0 and the other counters at their maximum
 // (expcnt 7, lgkmcnt 15). Issued through the builtin rather than inline asm

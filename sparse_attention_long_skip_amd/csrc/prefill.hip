@@ -86,10 +86,7 @@ template <int N>
 struct StepParity {
   static constexpr int value = N;
 };
-template <bool B>
-struct Flag {
-  static constexpr bool value = B;
-};
+
 
 // BR: query rows per workgroup (BR / 32 waves). UW: waves per decision unit
 // (the query tile of Br = 32 * UW rows); a workgroup holds BR / (32 UW)
@@ -223,39 +220,26 @@ void prefill_kernel(PrefillArgs a) {
 
   // LDS-direct tile loads: this wave fills LPW consecutive 1 KiB blocks; LDS
   // slot s (16 B) holds row s / CPR, logical chunk (s % CPR) ^ swz(row).
-  // Per-lane source offsets are fixed; rows past L (last tile only) read
-  // row L-1 (finite data; those scores are masked and their P is 0).
+  // Per-lane source offsets are fixed; a tile is read through a buffer
+  // resource that ends at row L, so rows past L (last tile only) land as
+  // zeros (their scores are masked and their P is 0), with no per-lane
+  // clamp and no branch.
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  // Source offsets are in bytes from the tile's first row, as 32-bit
-  // unsigned values (a wave-uniform base plus a 32-bit offset per lane).
+  // Source offsets are in bytes from the tile's first row.
   uint32_t koff[LPW], voff[LPW];
-  int lrow[LPW];
 #pragma unroll
   for (int r = 0; r < LPW; ++r) {
     const int s = (w * LPW + r) * 64 + lane;
     const int rr = s / CPR;
-    lrow[r] = rr;
     koff[r] = (uint32_t)(rr * D + ((s % CPR) ^ swz_k<D>(rr)) * 8) * 2u;
     voff[r] = (uint32_t)(rr * D + ((s % CPR) ^ swz_v<D>(rr)) * 8) * 2u;
   }
-  // With branchy set the ragged last tile takes a separate loop; otherwise
-  // the clamp is applied to every tile (four integer ops per load), and no
-  // branch splits the block the loads sit in.
-  auto load_tile = [&](const uint16_t* src, int j, uint16_t* dst, const uint32_t* off, auto branchy)
-                       __attribute__((always_inline)) {
+  // The resource is built per tile with scalar instructions only.
+  auto load_tile = [&](const uint16_t* src, int j, uint16_t* dst, const uint32_t* off) __attribute__((always_inline)) {
     const int kb0 = j * BC;
-    const char* base = reinterpret_cast<const char*>(src + (size_t)kb0 * D);
-    if (decltype(branchy)::value && kb0 + BC <= L) {
+    const auto rs = make_rsrc(src + (size_t)kb0 * D, min(L - kb0, BC) * D * 2);
 #pragma unroll
-      for (int r = 0; r < LPW; ++r) load_lds16(base + off[r], dst + (wu * LPW + r) * 512);
-    } else {
-#pragma unroll
-      for (int r = 0; r < LPW; ++r) {
-        // over <= lrow[r], so the offset stays non-negative
-        const uint32_t over = (uint32_t)max(kb0 + lrow[r] - (L - 1), 0);
-        load_lds16(base + (off[r] - over * (uint32_t)(2 * D)), dst + (wu * LPW + r) * 512);
-      }
-    }
+    for (int r = 0; r < LPW; ++r) load_lds16_buf(rs, off[r], dst + (wu * LPW + r) * 512);
   };
 
   float m_run = -INFINITY;  // running max of raw q.k over visited tiles (the vote)
@@ -390,7 +374,7 @@ void prefill_kernel(PrefillArgs a) {
 
   int jcur = 0, jnext = 0;  // tiles at list positions tcur and tnext
   int tcur = advance(0, jcur);
-  if (tcur < n_list) load_tile(kp, jcur, k_lds0, koff, Flag<true>{});
+  if (tcur < n_list) load_tile(kp, jcur, k_lds0, koff);
   int tnext = tcur < n_list ? advance(tcur + 1, jnext) : n_list;
   int jprev = -1;  // tile of the previous position
   // One pipeline step per list position t (the loop runs t = 0 .. n, one
@@ -489,10 +473,10 @@ void prefill_kernel(PrefillArgs a) {
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        load_tile(vp, jprev, v_lds[0], voff, Flag<false>{});
+        load_tile(vp, jprev, v_lds[0], voff);
       } else {
         vpar ^= 1;
-        load_tile(vp, jprev, v_lds[vpar], voff, Flag<false>{});
+        load_tile(vp, jprev, v_lds[vpar], voff);
         // The scores of tile t (run even past the last tile, where they are
         // not used) overlap the last exponential chunk: keys 0..31 go to
         // s[0], already consumed, while chunk 3 reads s[1].
@@ -518,7 +502,7 @@ void prefill_kernel(PrefillArgs a) {
     // K(t+1) is issued after the scores of tile t: the loads queue behind
     // the other waves' loads while the matrix cores work (measured ~1%
     // faster than issuing them right after the vote).
-    if (tnext < n_list) load_tile(kp, jnext, k_nxt, koff, Flag<true>{});
+    if (tnext < n_list) load_tile(kp, jnext, k_nxt, koff);
     jprev = -1;
     if (have_cur) {
       const int j = jcur;
