@@ -36,3 +36,17 @@ def test_nm_combined_with_skip_rule():
     r = prefill_parity(x["q"], x["k"], x["v"], lam, 128, 64, True, nm=(2, 4), dense_sink=64,
                        dense_recent=128)
     print(f"lambda {lam:.3f}: skipped {r['skipped']}/{r['visited']} exempt {r['exempt']}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_nm_2of4_exact_ties(causal):
+    # duplicated key rows inside groups of 4 give exactly equal scores (the
+    # same products in the same order on both sides): two-way ties in every
+    # second group and a three-way tie in every fourth, so the lower key
+    # index decides which equal score is kept
+    x = synth.prefill_inputs(503, 7, 1, 4, 2, 600, 128)
+    k = x["k"].copy()
+    k[:, :, 1::8, :] = k[:, :, 2::8, :][:, :, : k[:, :, 1::8, :].shape[2], :]
+    k[:, :, 3::16, :] = k[:, :, 2::16, :][:, :, : k[:, :, 3::16, :].shape[2], :]
+    r = prefill_parity(x["q"], k, x["v"], -math.inf, 128, 64, causal, nm=(2, 4))
+    assert r["skipped"] == 0
