@@ -104,3 +104,16 @@ def test_tile_edges(L, d, Br):
     q, k, v = _inputs(202, L, 1, 4, 2, L, d)
     r = prefill_parity(q, k, v, -0.2, Br, 64, True)
     print(f"L={L} d={d} Br={Br}: skipped {r['skipped']}/{r['visited']} err {r['max_err_out']:.2e}")
+
+
+@pytest.mark.parametrize("d,Br", [(64, 64), (128, 128), (128, 32)])
+def test_growing_scores_rescale(d, Br):
+    # keys scaled up along the sequence: every few tiles a row max exceeds
+    # the exponentials' reference by more than 2^8, so O, the row sum and the
+    # pending P are rescaled many times per row, with and without skipping
+    q, k, v = _inputs(204, 5, 1, 2, 1, 900, d)
+    ramp = (1.0 + np.arange(900, dtype=np.float32) / 20.0)[None, None, :, None]
+    k = synth.bf16_bits(synth.bf16_to_f32(k) * ramp)
+    for lam in (-math.inf, -1.0):
+        r = prefill_parity(q, k, v, lam, Br, 64, True)
+        print(f"d={d} Br={Br} lambda={lam}: skipped {r['skipped']}/{r['visited']}")
