@@ -117,3 +117,15 @@ def test_growing_scores_rescale(d, Br):
     for lam in (-math.inf, -1.0):
         r = prefill_parity(q, k, v, lam, Br, 64, True)
         print(f"d={d} Br={Br} lambda={lam}: skipped {r['skipped']}/{r['visited']}")
+
+
+@pytest.mark.parametrize("d,Br", [(64, 64), (128, 128)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_odd_batch_and_group(d, Br, causal):
+    # B = 3, G = 3 (B * Hkv = 6 KV heads: the workgroups are dealt to the
+    # XCDs in groups of G), a ragged length and a skipping lambda
+    q, k, v = _inputs(206, d + causal, 3, 6, 2, 517, d)
+    m = oracle.prefill(q, k, v, -math.inf, Br, 64, causal, bits=True)["margin"]
+    lam = oracle.lambda_for_ratio(m, 0.4)
+    r = prefill_parity(q, k, v, lam, Br, 64, causal)
+    print(f"d={d} Br={Br} causal={causal} lam={lam:.3f}: skipped {r['skipped']}/{r['visited']}")
