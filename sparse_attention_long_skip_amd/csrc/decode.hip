@@ -42,8 +42,12 @@ struct DecodeArgs {
   float inv_sqrt_d;
 };
 
+// Two waves per SIMD where the registers allow it without spilling (the
+// K prefetch and V rows of one wave are already many bytes in flight; a
+// second wave hides one wave's vector P.V behind the other's loads).
 template <int D, int G>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((D == 128 ? G <= 4 : G <= 8) ? 2 : 1)))
+void decode_split_kernel(DecodeArgs a) {
   constexpr int NKK = D / 16;
   constexpr int CPR = D / 8;     // 16-byte chunks per V row
   constexpr int RG = 64 / CPR;   // row groups across the wave
