@@ -25,10 +25,12 @@ def test_dense_and_calibrated_small(d, T):
     print(f"d={d} T={T} lam={lam:.3f} skipped {r['skipped']}/{r['visited']} exempt {r['exempt']}")
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
-def test_group_sizes(G):
+def test_group_sizes(G, d):
+    # every (d, G) instance, including those at one and at two waves per SIMD
     Hkv = 2
-    y = synth.decode_inputs(301, G, 2, G * Hkv, Hkv, 2048, 128, 1500, 2048)
+    y = synth.decode_inputs(301, G + d, 2, G * Hkv, Hkv, 2048, d, 1500, 2048)
     for lam in (-math.inf, -0.5):
         decode_parity(y, lam, 8)
 
