@@ -350,6 +350,37 @@ def extra_nm(args, torch, np, ssa, synth):
     return {"workload": "N:M 2:4 sparse softmax, 16K GQA shape, dense sink 64 + recent 256 tokens", "runs": rows}
 
 
+def extra_warp_units(args, torch, np, ssa, synth):
+    """Br = 32 decision units (the per-warp variant) on the 16K GQA shape,
+    lambda calibrated to ~50% of the 32-row units' tiles skipped."""
+    from sparse_attention_long_skip_amd.calibrate import lambda_for_ratio
+    c = synth.CONFIGS[1]
+    x = synth.prefill_inputs(1, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"], frac=c["frac"])
+    q, k, v = (dev_bf16(x[n], torch, np) for n in ("q", "k", "v"))
+    del x
+    kw = dict(Br=32, Bc=c["Bc"], causal=True)
+    m = ssa.prefill(q, k, v, -math.inf, margins=True, lse=False, **kw)["tile_margin"].cpu().numpy()
+    lam = lambda_for_ratio(m, 0.5)
+    st = ssa.prefill(q, k, v, lam, stats=True, **kw)
+    torch.cuda.synchronize()
+    s = st["tile_state"].cpu().numpy()  # [B, Hq, L / 32, nK]
+    vis, kept = int((s != 0).sum()), int((s == 1).sum())
+    # four 32-row units share a 128-row workgroup: every wave computes the
+    # scores of the tiles the workgroup visits and the P.V of the tiles any
+    # of its units keeps
+    g = s.reshape(s.shape[0], s.shape[1], -1, 4, s.shape[-1])
+    wg_vis = int((g != 0).any(axis=3).sum())
+    wg_kept = int((g == 1).any(axis=3).sum())
+    out = torch.empty_like(q)
+    ms, ev = time_launches(lambda: ssa.prefill(q, k, v, lam, out=out, **kw), 10, 3, torch)
+    ex = 2.0 * 32 * 64 * c["d"] * 4 * (wg_vis + wg_kept)
+    return {"workload": "Br=32 decision units (per-warp skip), 16K GQA shape, lambda calibrated to ~50% unit skip",
+            "lambda": round(lam, 5), "ms": round(ms, 4), "skip_pct": round(100.0 * (vis - kept) / vis, 3),
+            "pv_tiles_run_vs_kept": round(4 * wg_kept / max(kept, 1), 3),
+            "dense_equiv_tflops": round(dense_flops(c) / ms / 1e9, 1),
+            "mfma_frac_executed": round(ex / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -359,7 +390,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--only-main", action="store_true", help="skip extra and cpu baseline (profiling)")
     ap.add_argument("--leg", choices=["prefill_128k", "decode", "block_sparse_32k", "sparge_32k",
-                                      "vslash_32k", "nm_2of4_16k"],
+                                      "vslash_32k", "nm_2of4_16k", "warp_units_16k"],
                     help="run only this extra leg and print its JSON (profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the main leg, copy a 1 GiB buffer 5 times (HBM counter scale)")
@@ -378,7 +409,8 @@ def main():
     ssa.lib()
     torch.cuda.set_device(0)
     legs = {"prefill_128k": extra_128k, "decode": extra_decode, "block_sparse_32k": extra_sparse,
-            "sparge_32k": extra_sparge, "vslash_32k": extra_vslash, "nm_2of4_16k": extra_nm}
+            "sparge_32k": extra_sparge, "vslash_32k": extra_vslash, "nm_2of4_16k": extra_nm,
+            "warp_units_16k": extra_warp_units}
     if args.leg:
         print(json.dumps({args.leg: legs[args.leg](args, torch, np, ssa, synth)}), flush=True)
         return
