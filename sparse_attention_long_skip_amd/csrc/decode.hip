@@ -237,9 +237,12 @@ void decode_split_kernel(DecodeArgs a) {
   if (a.skip_counts && lane == 0) a.skip_counts[unit_s] = skipped;
 }
 
-// One workgroup per (query head, sequence): merge the split partials.
+// One workgroup per (query head, sequence): merge the split partials. The
+// partials are read 16 splits at a time with every load issued before the
+// first use (a loop that waited on each load in turn was latency-bound).
 template <int D>
 __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int U = 16;
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
   const int t = threadIdx.x;
@@ -247,29 +250,46 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
   const int ntiles = (n + BC - 1) / BC;
   const int nsp = (ntiles + a.T - 1) / a.T;
   const size_t base = ((size_t)b * a.Hq + hq) * a.nS;
-  // lse_s = m_s / sqrt(d) + ln l_s over live splits.
-  float top = -INFINITY;
-  for (int s = 0; s < nsp; ++s) {
-    const float m = a.ws_ml[(base + s) * 2];
-    const float l = a.ws_ml[(base + s) * 2 + 1];
-    if (l > 0.f) top = fmaxf(top, m * a.inv_sqrt_d + __logf(l));
-  }
-  float tot = 0.f;
-  if (top > -INFINITY) {
-    for (int s = 0; s < nsp; ++s) {
-      const float m = a.ws_ml[(base + s) * 2];
-      const float l = a.ws_ml[(base + s) * 2 + 1];
-      if (l > 0.f) tot += __expf(m * a.inv_sqrt_d + __logf(l) - top);
+  // lse = log sum_s exp(lse_s), lse_s = m_s / sqrt(d) + ln l_s over the
+  // splits with l_s > 0 (running max and rescaled sum, one split at a time).
+  float top = -INFINITY, tot = 0.f;
+  for (int s0 = 0; s0 < nsp; s0 += U) {
+    float mm[U], ll[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = s0 + u < nsp;
+      mm[u] = ok ? a.ws_ml[(base + s0 + u) * 2] : 0.f;
+      ll[u] = ok ? a.ws_ml[(base + s0 + u) * 2 + 1] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ll[u] > 0.f) {
+        const float x = mm[u] * a.inv_sqrt_d + __logf(ll[u]);
+        if (x > top) {
+          tot = tot * __expf(top - x) + 1.f;
+          top = x;
+        } else {
+          tot += __expf(x - top);
+        }
+      }
     }
   }
   const float lse = (tot > 0.f) ? top + __logf(tot) : -INFINITY;
   if (t < D) {
     float acc = 0.f;
     if (tot > 0.f) {
-      for (int s = 0; s < nsp; ++s) {
-        const float m = a.ws_ml[(base + s) * 2];
-        const float l = a.ws_ml[(base + s) * 2 + 1];
-        if (l > 0.f) acc += __expf(m * a.inv_sqrt_d - lse) * a.ws_o[(base + s) * D + t];
+      for (int s0 = 0; s0 < nsp; s0 += U) {
+        float mm[U], ll[U], oo[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const bool ok = s0 + u < nsp;
+          mm[u] = ok ? a.ws_ml[(base + s0 + u) * 2] : 0.f;
+          ll[u] = ok ? a.ws_ml[(base + s0 + u) * 2 + 1] : 0.f;
+          oo[u] = ok ? a.ws_o[(base + s0 + u) * D + t] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (ll[u] > 0.f) acc += __expf(mm[u] * a.inv_sqrt_d - lse) * oo[u];
       }
     }
     const __bf16 r = (__bf16)acc;
