@@ -379,8 +379,9 @@ void prefill_kernel(PrefillArgs a) {
   int jprev = -1;  // tile of the previous position
   // One pipeline step per list position t (the loop runs t = 0 .. n, one
   // barrier each): vote of tile t-1; if kept, P.V of the previous kept tile
-  // with the exponentials of tile t-1, then V(t-1); scores of tile t; K(t+1);
-  // row max and wave flag of tile t. buf = step parity selects the K buffers.
+  // with the exponentials of tile t-1 and the K(t+1) loads, then V(t-1);
+  // scores of tile t (K(t+1) after them when nothing was kept); row max and
+  // wave flag of tile t. buf = step parity selects the K buffers.
   auto step = [&](auto buf_c) __attribute__((always_inline)) -> bool {
     constexpr int buf = decltype(buf_c)::value;
     uint16_t* const k_cur = buf == 0 ? k_lds0 : k_lds1;  // K(t), read by the scores
@@ -457,10 +458,24 @@ void prefill_kernel(PrefillArgs a) {
       const float mc = !keep_mine ? INFINITY : (m_ref == -INFINITY ? 0.f : m_ref * a.c_log2);
       const uint16_t* vt = v_lds[VSINGLE ? 0 : vpar];
       float psum = 0.f;
+      // The K(t+1) loads go out one share after each P.V chunk, so they
+      // queue while the matrix cores work. Past the last position the
+      // resource is empty and the loads write zeros into the free buffer
+      // (no branch splits the block).
+      const bool kn = tnext < n_list;
+      const int kb0n = kn ? jnext * BC : 0;
+      const auto rsk = make_rsrc(kp + (size_t)kb0n * D, kn ? min(L - kb0n, BC) * D * 2 : 0);
+      auto k_share = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < LPW; ++r)
+          if (r * 4 / LPW == c) load_lds16_buf(rsk, koff[r], k_nxt + (wu * LPW + r) * 512);
+      };
       pv_chunk(vt, 0);
+      k_share(0);
 #pragma unroll
       for (int c = 0; c < 3; ++c) {
         pv_chunk(vt, c + 1);
+        k_share(c + 1);
         exp_chunk(c, mc, psum);
       }
       if constexpr (VSINGLE) {
@@ -499,10 +514,10 @@ void prefill_kernel(PrefillArgs a) {
           s[kb] = mfma32(ka, qf[kk], s[kb]);
         }
     }
-    // K(t+1) is issued after the scores of tile t: the loads queue behind
-    // the other waves' loads while the matrix cores work (measured ~1%
-    // faster than issuing them right after the vote).
-    if (tnext < n_list) load_tile(kp, jnext, k_nxt, koff);
+    // Without a kept tile, K(t+1) is issued after the scores of tile t: the
+    // loads queue behind the other waves' loads while the matrix cores work
+    // (measured ~1% faster than issuing them right after the vote).
+    if (!keep1 && tnext < n_list) load_tile(kp, jnext, k_nxt, koff);
     jprev = -1;
     if (have_cur) {
       const int j = jcur;
