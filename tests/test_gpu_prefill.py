@@ -131,35 +131,35 @@ def test_odd_batch_and_group(d, Br, causal):
     print(f"d={d} Br={Br} causal={causal} lam={lam:.3f}: skipped {r['skipped']}/{r['visited']}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_block_list_any_order(d):
+@pytest.mark.parametrize("d,Br", [(64, 64), (128, 64), (128, 128)])
+def test_block_list_any_order(d, Br):
     # lists in shuffled and in descending order, with more than 64 entries
     # (the list is read 64 entries per load), invalid entries mixed in: the
     # visit order sets the running max and so the skip decisions
     L = 64 * 90
     q, k, v = _inputs(207, d, 1, 2, 1, L, d)
-    nQ = L // 64
+    nQ = L // Br
     rng = np.random.default_rng(1)
     mb = 96
     idx = np.full((1, 2, nQ, mb), -1, np.int32)
     cnt = np.zeros((1, 2, nQ), np.int32)
     for h in range(2):
         for i in range(nQ):
-            tiles = list(range(i + 1))
+            tiles = list(range((i + 1) * Br // 64))
             if h == 0:
                 rng.shuffle(tiles)
             else:
                 tiles = tiles[::-1]
             if i % 7 == 3:
-                tiles.insert(len(tiles) // 2, nQ + 5)  # out of range
-                tiles.insert(1, i + 1)                 # above the causal limit
+                tiles.insert(len(tiles) // 2, L // 64 + 5)   # out of range
+                tiles.insert(1, (i + 1) * Br // 64)          # above the causal limit
             idx[0, h, i, :len(tiles)] = tiles[:mb]
             cnt[0, h, i] = min(len(tiles), mb)
-    units = [(0, h, i) for h in range(2) for i in (0, 3, 45, 70, 80, 89)]
-    m = oracle.prefill(q, k, v, -math.inf, 64, 64, True, bits=True, block_idx=idx, block_cnt=cnt,
+    units = [(0, h, i) for h in range(2) for i in sorted({0, 3, 45, 70, 80, 89, nQ - 1} & set(range(nQ)))]
+    m = oracle.prefill(q, k, v, -math.inf, Br, 64, True, bits=True, block_idx=idx, block_cnt=cnt,
                        units=units)["margin"]
     for lam in (-math.inf, oracle.lambda_for_ratio(m, 0.4)):
-        r = prefill_parity(q, k, v, lam, 64, 64, True, block_idx=idx, block_cnt=cnt, units=units)
+        r = prefill_parity(q, k, v, lam, Br, 64, True, block_idx=idx, block_cnt=cnt, units=units)
         print(f"d={d} lambda={lam:.3f}: skipped {r['skipped']}/{r['visited']}")
         if lam > -math.inf:
             assert r["skipped"] > 0
