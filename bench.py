@@ -215,7 +215,7 @@ def extra_decode(args, torch, np, ssa, synth):
     io = 2.0 * 2 * c["B"] * c["Hq"] * d
     wsb = 2.0 * 4 * c["B"] * c["Hq"] * sum(math.ceil(math.ceil(n / Bc) / T) for n in lens) * (d + 2)
     loaded = k_bytes + v_bytes + io + wsb
-    return {"workload": "decode B=32 Hq=32 Hkv=8 d=128 lens U[16K,32K] split 32 tiles",
+    return {"workload": f"decode B=32 Hq=32 Hkv=8 d=128 lens U[16K,32K] split {T} tiles",
             "lambda": round(lam, 5), "tokens_per_s": round(c["B"] / (ms * 1e-3), 1), "ms": round(ms, 4),
             "event_ms": round(ev, 4), "skip_pct_v_tiles": round(100.0 * (vis - kept) / vis, 3),
             "loaded_bytes": loaded, "hbm_gbs": round(loaded / (ev * 1e-3) / 1e9, 1),
