@@ -31,9 +31,10 @@
 //      wait for this wave's loads; barrier (K(t), the last kept V, flags(t-1)
 //      visible); workgroup vote of tile t-1 (OR of the per-wave ballots); if
 //      tile t-1 is kept: P.V of the previous kept tile interleaved with
-//      exp -> P(t-1) (bf16 registers), chunk by chunk, then the V(t-1)
-//      loads; scores of tile t (MFMA); the K(t+1) loads; row max, gap
-//      against the running max, wave ballot.
+//      exp -> P(t-1) (bf16 registers), chunk by chunk, with the K(t+1)
+//      loads, then the V(t-1) loads and the scores of tile t; otherwise the
+//      scores of tile t, then the K(t+1) loads; row max, gap against the
+//      running max, wave ballot.
 //    So V is fetched only for kept tiles and has at least a whole step to
 //    land, and the exponentials run in the shadow of the matrix work.
 //  * The exponentials use a reference max that lags the running max: O and
