@@ -480,16 +480,20 @@ void prefill_kernel(PrefillArgs a) {
         exp_chunk(c, mc, psum);
       }
       if constexpr (VSINGLE) {
-        exp_chunk(3, mc, psum);
         // Every wave is done reading the V buffer before any wave loads
         // V(t-1) into it: this wave's LDS reads have returned (lgkmcnt 0;
         // vmcnt and expcnt left at their maximum), then a plain barrier (a
-        // full __syncthreads() would also wait for the K(t+1) loads).
+        // full __syncthreads() would also wait for the K(t+1) loads). The
+        // scores of tile t then overlap the last exponential chunk, as
+        // below.
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         load_tile(vp, jprev, v_lds[0], voff);
+        scores_half(k_cur, 0);
+        exp_chunk(3, mc, psum);
+        scores_half(k_cur, 1);
       } else {
         vpar ^= 1;
         load_tile(vp, jprev, v_lds[vpar], voff);
@@ -502,7 +506,7 @@ void prefill_kernel(PrefillArgs a) {
       }
       l_acc += psum;
     }
-    if (have_cur && (VSINGLE || !keep1)) {
+    if (have_cur && !keep1) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
