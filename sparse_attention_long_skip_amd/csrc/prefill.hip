@@ -637,8 +637,12 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   a.Hkv = p.Hkv;
   a.L = p.L;
   // Workgroup rows: Br = 32 units run four to a 128-row workgroup (per-wave
-  // votes); Br = 64 and 128 units run one per workgroup.
-  const int br_wg = p.Br == 32 ? 128 : p.Br;
+  // votes); at d = 128 without a block list, Br = 64 units run two to a
+  // 128-row workgroup (a 64-row workgroup holds the same 64 KiB of K/V
+  // tiles, so only one of its waves would fit per SIMD); otherwise one unit
+  // per workgroup.
+  const bool pair64 = p.Br == 64 && p.d == 128 && p.block_idx == nullptr;
+  const int br_wg = (p.Br == 32 || pair64) ? 128 : p.Br;
   a.nQ = (p.L + br_wg - 1) / br_wg;
   a.nQ_unit = (p.L + p.Br - 1) / p.Br;
   a.nK = (p.L + p.Bc - 1) / p.Bc;
@@ -670,7 +674,7 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
     if (p.d == 128) return launch<128, 128, 4>(a, stream);
     if (p.d == 64) return launch<64, 128, 4>(a, stream);
   } else if (p.Br == 64) {
-    if (p.d == 128) return launch<128, 64, 2>(a, stream);
+    if (p.d == 128) return pair64 ? launch<128, 128, 2>(a, stream) : launch<128, 64, 2>(a, stream);
     if (p.d == 64) return launch<64, 64, 2>(a, stream);
   }
   return hipErrorInvalidValue;

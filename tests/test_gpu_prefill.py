@@ -27,7 +27,7 @@ def test_dense_small_ragged(d, Br, causal):
     assert r["skipped"] == 0
 
 
-@pytest.mark.parametrize("d,Br", [(64, 64), (128, 128)])
+@pytest.mark.parametrize("d,Br", [(64, 64), (128, 128), (128, 64)])
 def test_skip_small_gqa(d, Br):
     q, k, v = _inputs(201, 2, 2, 8, 2, 1000, d)
     B, Hq, L, _ = q.shape
@@ -98,7 +98,7 @@ def test_wave_granular_votes(d):
 
 
 @pytest.mark.parametrize("L", [1, 63, 64, 65, 127, 129, 191])
-@pytest.mark.parametrize("d,Br", [(64, 64), (128, 128), (128, 32)])
+@pytest.mark.parametrize("d,Br", [(64, 64), (128, 128), (128, 64), (128, 32)])
 def test_tile_edges(L, d, Br):
     # lengths at and around tile boundaries, GQA 4/2, a skipping lambda
     q, k, v = _inputs(202, L, 1, 4, 2, L, d)
@@ -119,7 +119,7 @@ def test_growing_scores_rescale(d, Br):
         print(f"d={d} Br={Br} lambda={lam}: skipped {r['skipped']}/{r['visited']}")
 
 
-@pytest.mark.parametrize("d,Br", [(64, 64), (128, 128)])
+@pytest.mark.parametrize("d,Br", [(64, 64), (128, 128), (128, 64)])
 @pytest.mark.parametrize("causal", [True, False])
 def test_odd_batch_and_group(d, Br, causal):
     # B = 3, G = 3 (B * Hkv = 6 KV heads: the workgroups are dealt to the
