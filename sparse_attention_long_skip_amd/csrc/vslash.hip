@@ -313,22 +313,42 @@ __global__ __launch_bounds__(SEL_T) void vs_select(VsArgs a) {
   int need = n;
   const bool take_all = n >= L;
   const bool by_rank = n > 0 && !take_all;
+  // Up to SEL_T * NR keys are read once into registers (all four passes
+  // then run on them); longer rows are re-read every pass.
+  constexpr int NR = 32;
+  const bool in_reg = L <= SEL_T * NR;
+  uint32_t ur[NR];
+  if (by_rank && in_reg) {
+#pragma unroll
+    for (int e = 0; e < NR; ++e) {
+      const int j = e * SEL_T + t;
+      ur[e] = j < L ? order_bits(x[j]) : 0u;
+    }
+  }
   if (by_rank) {
     for (int shift = 24; shift >= 0; shift -= 8) {
       for (int e = t; e < NCOPY * HS; e += SEL_T) hist[e] = 0;
       __syncthreads();
       int* mine = hist + (t & (NCOPY - 1)) * HS;
-      for (int b0 = 0; b0 < L; b0 += SEL_T * 8) {  // 8 loads in flight per thread
-        uint32_t u[8];
+      if (in_reg) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = b0 + e * SEL_T + t;
-          u[e] = j < L ? order_bits(x[j]) : 0u;
+        for (int e = 0; e < NR; ++e) {
+          const int j = e * SEL_T + t;
+          if (j < L && (ur[e] & mask) == thr) atomicAdd(&mine[(ur[e] >> shift) & 255], 1);
         }
+      } else {
+        for (int b0 = 0; b0 < L; b0 += SEL_T * 8) {  // 8 loads in flight per thread
+          uint32_t u[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = b0 + e * SEL_T + t;
-          if (j < L && (u[e] & mask) == thr) atomicAdd(&mine[(u[e] >> shift) & 255], 1);
+          for (int e = 0; e < 8; ++e) {
+            const int j = b0 + e * SEL_T + t;
+            u[e] = j < L ? order_bits(x[j]) : 0u;
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int j = b0 + e * SEL_T + t;
+            if (j < L && (u[e] & mask) == thr) atomicAdd(&mine[(u[e] >> shift) & 255], 1);
+          }
         }
       }
       __syncthreads();
