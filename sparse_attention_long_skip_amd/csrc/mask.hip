@@ -39,7 +39,9 @@ struct MaskArgs {
   const uint16_t* q;
   const uint16_t* k;
   float* qbar;  // [B, H, nB, D]
-  float* kbar;  // [B, H, nB, D]
+  float* kbar;  // mean keys [B, H, D / 4, nB, 4] (4-channel groups, so that
+                //   consecutive blocks are adjacent); compressed windows
+                //   [B, H, nW, D]
   int32_t* block_idx;
   int32_t* block_cnt;
   float* block_scores;
@@ -120,7 +122,10 @@ __global__ __launch_bounds__(256) void pool_kernel(MaskArgs a) {
       sm += part[0][g][t];
       if constexpr (SIM) sn += part[SIM ? 1 : 0][g][t];
     }
-    dst[t] = sm / n;
+    if (is_k)  // 4-channel groups: the selection reads one group of 64 blocks per load
+      a.kbar[((hb * (D / 4) + t / 4) * a.nB + blk) * 4 + (t & 3)] = sm / n;
+    else
+      dst[t] = sm / n;
     un = sn / n;  // channel t of the mean unit row
   }
   if constexpr (SIM) {
@@ -229,13 +234,15 @@ __global__ __launch_bounds__(256) void select_kernel(MaskArgs a) {
     for (int q = 0; q < QPB; ++q) acc[q] = -INFINITY;
     const int nwin = COMP ? min(kWinPerBlock, a.nW - c * kWinPerBlock) : 1;
     for (int w = 0; w < nwin; ++w) {
-      const float* kr = kb + (size_t)(COMP ? c * kWinPerBlock + w : c) * D;
+      // compressed windows are rows of D; mean keys come in 4-channel groups
+      const float* kr = COMP ? kb + (size_t)(c * kWinPerBlock + w) * D : kb + (size_t)c * 4;
+      const size_t kstep = COMP ? 4 : (size_t)a.nB * 4;
       float part[QPB];
 #pragma unroll
       for (int q = 0; q < QPB; ++q) part[q] = 0.f;
 #pragma unroll 4
       for (int e = 0; e < D; e += 4) {
-        const f32x4 kx = *reinterpret_cast<const f32x4*>(kr + e);
+        const f32x4 kx = *reinterpret_cast<const f32x4*>(kr + (size_t)(e / 4) * kstep);
 #pragma unroll
         for (int q = 0; q < QPB; ++q) {
           part[q] = fmaf(qv[q][e], kx[0], part[q]);
