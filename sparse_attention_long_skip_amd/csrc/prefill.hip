@@ -348,28 +348,31 @@ void prefill_kernel(PrefillArgs a) {
         float x[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = s[kb][q4 * 4 + e];
-        bool keep[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int g0 = (a.nm_m == 2) ? (e & 2) : 0;
-          int rank = 0;
-#pragma unroll
-          for (int f = 0; f < 4; ++f) {
-            const bool same = (a.nm_m == 2) ? ((f & 2) == g0) : true;
-            if (f != e && same) rank += (x[f] > x[e] || (x[f] == x[e] && f < e)) ? 1 : 0;
-          }
-          keep[e] = rank < a.nm_n;
+        // rank of e = members of its group that beat it (higher score, or
+        // equal score and lower key). For e < f one comparison decides the
+        // pair: f beats e iff x[f] > x[e], else e beats f (scores are never
+        // NaN).
+        const bool c01 = x[1] > x[0], c23 = x[3] > x[2];
+        int r0 = c01, r1 = !c01, r2 = c23, r3 = !c23;
+        if (a.nm_m == 4) {
+          const bool c02 = x[2] > x[0], c03 = x[3] > x[0], c12 = x[2] > x[1], c13 = x[3] > x[1];
+          r0 += c02 + c03;
+          r1 += c12 + c13;
+          r2 += !c02 + !c12;
+          r3 += !c03 + !c13;
         }
+        const bool keep[4] = {r0 < a.nm_n, r1 < a.nm_n, r2 < a.nm_n, r3 < a.nm_n};
+        bool keepx[4] = {keep[0], keep[1], keep[2], keep[3]};
         if (exempt_here) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int key = kbase + kb * 32 + q4 * 8 + h * 4 + e;
-            keep[e] = keep[e] || key < a.dense_sink || (row - a.dense_recent < key && key <= row);
+            keepx[e] = keepx[e] || key < a.dense_sink || (row - a.dense_recent < key && key <= row);
           }
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (!keep[e]) s[kb][q4 * 4 + e] = -INFINITY;
+          if (!keepx[e]) s[kb][q4 * 4 + e] = -INFINITY;
       }
   };
 
