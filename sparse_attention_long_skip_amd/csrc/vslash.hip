@@ -67,7 +67,7 @@ __device__ __forceinline__ uint32_t order_bits(float x) {
 template <int D, int PASS>
 __global__ __launch_bounds__(256) void vs_pass(VsArgs a) {
   constexpr int KS = D / 16;  // MFMA k-steps
-  __shared__ float A_lds[PASS ? 64 : 1][CH + 1];
+  __shared__ float A_lds[PASS ? 32 : 1][CH + 1];  // one half (32 query rows) of the A tile
   __shared__ float red[4][64][2];
   const int chunk = blockIdx.x;
   const size_t hb = (size_t)blockIdx.z * a.H + blockIdx.y;
@@ -102,49 +102,97 @@ __global__ __launch_bounds__(256) void vs_pass(VsArgs a) {
     }
   }
 
-  for (int g = wv; g < CH / 32; g += 4) {
+  // S^T tile of keys g * 32 .. g * 32 + 31 of the chunk against both row blocks
+  auto scores = [&](int g, f32x16* acc) __attribute__((always_inline)) {
     const int jk = j0 + g * 32 + col;  // this lane's key for the A operand
     bf16x8 kop[KS];
     const uint16_t* krow = kp + (size_t)(jk < a.L ? jk : 0) * D + 8 * h;
 #pragma unroll
     for (int s = 0; s < KS; ++s) kop[s] = jk < a.L ? as_bf16x8(load16(krow + 16 * s)) : bf16x8{};
-    f32x16 acc[2] = {f32x16{}, f32x16{}};
+    acc[0] = f32x16{};
+    acc[1] = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       acc[0] = mfma32(kop[s], qop[0][s], acc[0]);
       acc[1] = mfma32(kop[s], qop[1][s], acc[1]);
     }
+  };
+  if constexpr (PASS == 1) {
+    // The A tile goes through LDS one 32-row half at a time (half the LDS,
+    // so twice the workgroups per CU); the column and diagonal sums carry
+    // their running totals across the halves, adding rows in the same
+    // increasing order as over the whole tile.
+    constexpr int NG = CH / 32 / 4;  // key groups per wave
+    f32x16 acc[NG][2];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) scores(wv + 4 * gi, acc[gi]);
+    float csum = 0.f;
+    float dsum[2] = {0.f, 0.f};  // diagonals e = t and e = t + 256
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      __syncthreads();  // the previous half has been read
+      const int i = rb * 32 + col;
+      const int p = a.L - a.R + i;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        const int g = wv + 4 * gi;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jl = g * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+          const int j = j0 + jl;
+          const bool ok = i < a.R && j < a.L && j <= p;
+          A_lds[col][jl] = ok ? fast_exp2(acc[gi][rb][r] * a.c_log2 - mrow[rb]) * invl[rb] : 0.f;
+        }
+      }
+      __syncthreads();
+      const int r_lo = rb * 32, r_hi = min(a.R, rb * 32 + 32);  // rows of this half
+      if (j0 + t < a.L)
+        for (int r = r_lo; r < r_hi; ++r) csum += A_lds[r - r_lo][t];
+      // diagonal e meets row r at chunk column r + CH - 1 - e
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int e = t + 256 * k;
+        if (e < CH + a.R - 1) {
+          const int i0 = max(max(0, e - CH + 1), r_lo);
+          const int i1 = min(min(a.R - 1, e), r_hi - 1);
+          for (int r = i0; r <= i1; ++r) dsum[k] += A_lds[r - r_lo][r + CH - 1 - e];
+        }
+      }
+    }
+    if (j0 + t < a.L) a.v[hb * a.L + j0 + t] = csum;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = t + 256 * k;
+      if (e < CH + a.R - 1) a.spart[(hb * a.nchunk + chunk) * SPW + e] = dsum[k];
+    }
+    return;
+  }
+
+  // pass 0: online (max, sum) of every row over this chunk's keys
+  for (int g = wv; g < CH / 32; g += 4) {
+    f32x16 acc[2];
+    scores(g, acc);
     // lane holds query row rb * 32 + col; register r holds key
     // g * 32 + 8 (r / 4) + 4 h + r % 4 of the chunk
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int i = rb * 32 + col;
       const int p = a.L - a.R + i;
-      if constexpr (PASS == 0) {
-        float mx = m_run[rb];
+      float mx = m_run[rb];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + g * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+        if (i < a.R && j < a.L && j <= p) mx = fmaxf(mx, acc[rb][r] * a.c_log2);
+      }
+      if (mx != -INFINITY) {
+        float l = m_run[rb] == -INFINITY ? 0.f : l_run[rb] * fast_exp2(m_run[rb] - mx);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = j0 + g * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-          if (i < a.R && j < a.L && j <= p) mx = fmaxf(mx, acc[rb][r] * a.c_log2);
+          if (i < a.R && j < a.L && j <= p) l += fast_exp2(acc[rb][r] * a.c_log2 - mx);
         }
-        if (mx != -INFINITY) {
-          float l = m_run[rb] == -INFINITY ? 0.f : l_run[rb] * fast_exp2(m_run[rb] - mx);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = j0 + g * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-            if (i < a.R && j < a.L && j <= p) l += fast_exp2(acc[rb][r] * a.c_log2 - mx);
-          }
-          m_run[rb] = mx;
-          l_run[rb] = l;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int jl = g * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-          const int j = j0 + jl;
-          const bool ok = i < a.R && j < a.L && j <= p;
-          A_lds[i][jl] = ok ? fast_exp2(acc[rb][r] * a.c_log2 - mrow[rb]) * invl[rb] : 0.f;
-        }
+        m_run[rb] = mx;
+        l_run[rb] = l;
       }
     }
   }
@@ -178,26 +226,6 @@ __global__ __launch_bounds__(256) void vs_pass(VsArgs a) {
       o[0] = mx;
       o[1] = l;
     }
-  } else {
-  __syncthreads();
-  // column sums: complete for this chunk's keys
-  {
-    const int j = j0 + t;
-    if (j < a.L) {
-      float sum = 0.f;
-      for (int i = 0; i < a.R; ++i) sum += A_lds[i][t];
-      a.v[hb * a.L + j] = sum;
-    }
-  }
-  // diagonal sums: offset o = L - R - (j0 + CH - 1) + e meets row i at chunk
-  // column i + CH - 1 - e
-  for (int e = t; e < CH + a.R - 1; e += 256) {
-    const int i0 = max(0, e - CH + 1);
-    const int i1 = min(a.R - 1, e);
-    float sum = 0.f;
-    for (int i = i0; i <= i1; ++i) sum += A_lds[i][i + CH - 1 - e];
-    a.spart[(hb * a.nchunk + chunk) * SPW + e] = sum;
-  }
   }
 }
 
