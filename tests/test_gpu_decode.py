@@ -68,3 +68,14 @@ def test_length_tile_edges(lens):
     y = synth.decode_inputs(302, sum(lens), len(lens), 8, 2, 2048, 128, 1, 2048, seqlens=lens)
     r = decode_parity(y, -0.5, 4)
     print(f"lens={lens}: skipped {r['skipped']}/{r['visited']}")
+
+
+@pytest.mark.parametrize("lens", [[1535, 1536, 1537, 3072], [64 * 24 * 3 - 1, 1, 64 * 24 + 63, 4100]])
+def test_split_boundaries_24(lens):
+    # splits of 24 tiles (1536 keys): lengths at and around split ends, the
+    # last split partial or a single key long; two query heads per KV head
+    y = synth.decode_inputs(304, len(lens), len(lens), 4, 2, 4608, 128, 1, 4608, seqlens=lens)
+    for lam in (-math.inf, -0.4):
+        r = decode_parity(y, lam, 24)
+        print(f"lens={lens} lambda={lam}: skipped {r['skipped']}/{r['visited']}")
+
