@@ -38,6 +38,22 @@ def test_config1_gqa_16k_half_skipped():
     assert 0.3 < r["skipped"] / r["visited"] < 0.7
 
 
+@pytest.mark.parametrize("Br", [64, 32])
+def test_config1_shape_smaller_units(Br):
+    # the 16K GQA shape with 64- and 32-row decision units (several units per
+    # 128-row workgroup), ~50% of the sampled units' tiles skipped
+    c = synth.CONFIGS[1]
+    x = synth.prefill_inputs(1, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"], frac=c["frac"])
+    nQ = math.ceil(c["L"] / Br)
+    units = _units(np.random.default_rng(13 + Br), c["B"], c["Hq"], nQ, 10)
+    m = oracle.prefill(x["q"], x["k"], x["v"], -math.inf, Br, c["Bc"], True, units=units, bits=True)["margin"]
+    lam = oracle.lambda_for_ratio(m, c["target_skip"])
+    r = prefill_parity(x["q"], x["k"], x["v"], lam, Br, c["Bc"], True, units=units)
+    print(f"16K shape Br={Br}: lambda {lam:.4f}, sampled skip {r['skipped']}/{r['visited']}, "
+          f"exempt {r['exempt']}, max err {r['max_err_out']:.2e}")
+    assert 0.3 < r["skipped"] / r["visited"] < 0.7
+
+
 @pytest.mark.parametrize("lam", [-3.0, -9.0])
 def test_config3_128k_threshold_sweep_ends(lam):
     c = synth.CONFIGS[3]
