@@ -12,7 +12,7 @@ from parity import prefill_parity
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("d,Br", [(64, 64), (128, 128)])
+@pytest.mark.parametrize("d,Br", [(64, 64), (128, 128), (128, 64), (64, 128), (128, 32)])
 @pytest.mark.parametrize("n,m", [(2, 4), (1, 4), (3, 4), (1, 2)])
 def test_nm_dense_small(d, Br, n, m):
     x = synth.prefill_inputs(500, n * 10 + m, 1, 2, 1, 333, d)
