@@ -486,27 +486,22 @@ void prefill_kernel(PrefillArgs a) {
         // Every wave is done reading the V buffer before any wave loads
         // V(t-1) into it: this wave's LDS reads have returned (lgkmcnt 0;
         // vmcnt and expcnt left at their maximum), then a plain barrier (a
-        // full __syncthreads() would also wait for the K(t+1) loads). The
-        // scores of tile t then overlap the last exponential chunk, as
-        // below.
+        // full __syncthreads() would also wait for the K(t+1) loads).
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         load_tile(vp, jprev, v_lds[0], voff);
-        scores_half(k_cur, 0);
-        exp_chunk(3, mc, psum);
-        scores_half(k_cur, 1);
       } else {
         vpar ^= 1;
         load_tile(vp, jprev, v_lds[vpar], voff);
-        // The scores of tile t (run even past the last tile, where they are
-        // not used) overlap the last exponential chunk: keys 0..31 go to
-        // s[0], already consumed, while chunk 3 reads s[1].
-        scores_half(k_cur, 0);
-        exp_chunk(3, mc, psum);
-        scores_half(k_cur, 1);
       }
+      // The scores of tile t (run even past the last tile, where they are
+      // not used) overlap the last exponential chunk: keys 0..31 go to s[0],
+      // already consumed, while chunk 3 reads s[1].
+      scores_half(k_cur, 0);
+      exp_chunk(3, mc, psum);
+      scores_half(k_cur, 1);
       l_acc += psum;
     }
     if (have_cur && !keep1) {
