@@ -98,6 +98,43 @@ def prefill_work(state, Br, Bc, d):
     return vis, kept, 2.0 * Br * Bc * d * (vis + kept)
 
 
+def visited_tiles_count(B, Hq, L, Br, Bc, causal, block_idx=None, block_cnt=None):
+    """Key tiles the prefill visits, summed over all decision units: every
+    tile up to the causal limit of the query tile (dense), or the list entries
+    that are in range and within the causal limit (block list). Host
+    arrays."""
+    import numpy as np
+    nQ, nK = -(-L // Br), -(-L // Bc)
+    last_row = np.minimum((np.arange(nQ) + 1) * Br, L) - 1
+    if block_idx is None:
+        per = (last_row // Bc + 1) if causal else np.full(nQ, nK)
+        return int(per.sum()) * B * Hq
+    idx = np.asarray(block_idx)
+    cnt = np.clip(np.asarray(block_cnt), 0, idx.shape[-1])
+    pos = np.arange(idx.shape[-1])
+    ok = (pos < cnt[..., None]) & (idx >= 0) & (idx < nK)
+    if causal:
+        ok &= idx * Bc <= last_row[None, None, :, None]
+    return int(ok.sum())
+
+
+def decode_loaded_bytes(lens, B, Hq, Hkv, d, Bc, T, kept_tiles):
+    """Algorithmic HBM bytes of one split-K decode call: K of every valid key
+    (bf16), V of every kept tile (bf16, a ragged last tile counted whole, as
+    its rows are read), q read and out written (bf16), lse written (fp32),
+    and the split partials -- d + 2 fp32 per (sequence, query head, split) --
+    written by the split kernel and read by the combine kernel."""
+    def ceil_div(a, b):
+        return -(-a // b)
+    lens = [max(int(n), 0) for n in lens]
+    k_bytes = 2 * d * Hkv * sum(lens)
+    v_bytes = 2 * d * Bc * int(kept_tiles)
+    io = 2 * (2 * B * Hq * d) + 4 * B * Hq
+    splits = sum(ceil_div(ceil_div(n, Bc), T) for n in lens)
+    ws = 2 * 4 * Hq * splits * (d + 2)
+    return k_bytes + v_bytes + io + ws
+
+
 def bench_prefill(cfg_id, args, torch, np, ssa, synth, lam=None, target=None, seed=0):
     from sparse_attention_long_skip_amd.calibrate import calibrate_prefill
     c = synth.CONFIGS[cfg_id]
@@ -113,16 +150,55 @@ def bench_prefill(cfg_id, args, torch, np, ssa, synth, lam=None, target=None, se
     return res
 
 
-def run_prefill(p, lam, steps, warmup, torch, ssa):
+def run_prefill(p, lam, steps, warmup, torch, ssa, check_stats=True):
+    """Time the plain prefill instance (out, lse and per-unit skip counts).
+    The kept-tile count comes from the skip counts of the last timed launch;
+    with ``check_stats`` a statistics launch (per-tile decisions) beforehand
+    must agree with it. Returns (visited, kept, ms per step, event ms)."""
     c = p["cfg"]
     q, k, v = p["q"], p["k"], p["v"]
-    st = ssa.prefill(q, k, v, lam, Br=c["Br"], Bc=c["Bc"], causal=c["causal"], stats=True)
-    torch.cuda.synchronize()
-    state = st["tile_state"].cpu().numpy()
+    B, Hq, L, d = q.shape
     out = torch.empty_like(q)
-    fn = lambda: ssa.prefill(q, k, v, lam, Br=c["Br"], Bc=c["Bc"], causal=c["causal"], out=out)
+    counts = torch.empty((B, Hq, -(-L // c["Br"])), dtype=torch.int32, device=q.device)
+    fn = lambda: ssa.prefill(q, k, v, lam, Br=c["Br"], Bc=c["Bc"], causal=c["causal"], out=out,
+                             skip_counts=counts)
     ms, ev_ms = time_launches(fn, steps, warmup, torch)
-    return state, ms, ev_ms
+    vis = visited_tiles_count(B, Hq, L, c["Br"], c["Bc"], c["causal"])
+    kept = vis - int(counts.sum().item())
+    if check_stats:
+        st = ssa.prefill(q, k, v, lam, Br=c["Br"], Bc=c["Bc"], causal=c["causal"], stats=True, lse=False)
+        torch.cuda.synchronize()
+        s_vis, s_kept, _ = prefill_work(st["tile_state"].cpu().numpy(), c["Br"], c["Bc"], d)
+        if (s_vis, s_kept) != (vis, kept):
+            raise RuntimeError(f"timed launch counts ({vis}, {kept}) differ from the statistics launch "
+                               f"({s_vis}, {s_kept})")
+        del st
+    return vis, kept, ms, ev_ms
+
+
+def time_prefill_legs(q, k, v, lam, kw, steps, warmup, torch, ssa):
+    """Time the plain prefill instance with keyword arguments ``kw`` (tile
+    sizes, causal, block list or N:M). Kept tiles come from the timed
+    launches' own skip counts; a statistics launch must agree. Returns
+    (visited, kept, ms per step, event ms)."""
+    B, Hq, L, d = q.shape
+    Br = kw["Br"]
+    out = torch.empty_like(q)
+    counts = torch.empty((B, Hq, -(-L // Br)), dtype=torch.int32, device=q.device)
+    ms, ev = time_launches(lambda: ssa.prefill(q, k, v, lam, out=out, skip_counts=counts, **kw),
+                           steps, warmup, torch)
+    bi, bc = kw.get("block_idx"), kw.get("block_cnt")
+    vis = visited_tiles_count(B, Hq, L, Br, kw["Bc"], kw["causal"],
+                              None if bi is None else bi.cpu().numpy(),
+                              None if bc is None else bc.cpu().numpy())
+    kept = vis - int(counts.sum().item())
+    st = ssa.prefill(q, k, v, lam, stats=True, lse=False, **kw)
+    torch.cuda.synchronize()
+    s_vis, s_kept, _ = prefill_work(st["tile_state"].cpu().numpy(), Br, kw["Bc"], d)
+    if (s_vis, s_kept) != (vis, kept):
+        raise RuntimeError(f"timed launch counts ({vis}, {kept}) differ from the statistics launch "
+                           f"({s_vis}, {s_kept})")
+    return vis, kept, ms, ev
 
 
 def dense_flops(c):
@@ -130,38 +206,143 @@ def dense_flops(c):
     return 4.0 * c["d"] * c["B"] * c["Hq"] * L * (L + 1) / 2
 
 
-def cpu_baseline_prefill(cfg_id, lam, budget_s, np, synth):
-    """Time the oracle on a seeded sample of query tiles of the same workload."""
-    import oracle
+# ---- CPU baseline: the fp64 oracle, in parallel worker processes ----------
+#
+# One process per core of this process's affinity set (at most 16), each with
+# single-threaded BLAS; every task is one decision unit (or one head) of the
+# same seeded workload, read from memory-mapped copies of the inputs. Tasks
+# run until the wall-clock budget is spent; the rate counts finished tasks.
+
+CPU_WORKERS_MAX = 16
+_W = {}
+
+
+def cpu_workers() -> int:
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        n = len(os.sched_getaffinity(0))
     except Exception:
-        threads = 1
+        n = os.cpu_count() or 1
+    return max(1, min(CPU_WORKERS_MAX, n))
+
+
+def _worker_init(paths):
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+    for name, path in paths.items():
+        _W[name] = np.load(path, mmap_mode="r")
+
+
+def _noop(x):
+    return x
+
+
+def _prefill_unit_task(args):
+    import oracle
+    unit, lam, Br, Bc, causal = args
+    oracle.prefill(_W["q"], _W["k"], _W["v"], lam, Br, Bc, causal, units=[unit], bits=True)
+    return unit
+
+
+def _decode_unit_task(args):
+    import oracle
+    unit, lam, Bc, T = args
+    oracle.decode(_W["q"], _W["k_cache"], _W["v_cache"], _W["seqlens"], lam, Bc, T, units=[unit],
+                  bits=True)
+    return unit
+
+
+def _sparse_head_task(args):
+    """Block mask of one head, then the block-sparse prefill of its query
+    blocks; returns the two times."""
+    import oracle
+    h, lam, pool, topk, sink, window = args
+    q = _W["q"][:, h:h + 1]
+    k = _W["k"][:, h:h + 1]
+    t0 = time.perf_counter()
+    m = oracle.block_mask(q, k, pool, topk, sink, window, bits=True)
+    t1 = time.perf_counter()
+    oracle.prefill(q, k, _W["v"][:, h:h + 1], lam, pool, pool, True, block_idx=m["block_idx"],
+                   block_cnt=m["block_cnt"], bits=True)
+    return h, t1 - t0, time.perf_counter() - t1
+
+
+def run_cpu_pool(arrays: dict, fn, tasks, budget_s: float):
+    """Run ``fn`` over ``tasks`` in worker processes until the budget is
+    spent. Returns (finished task results, wall seconds, workers)."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+    import numpy as np
+    tmp = tempfile.mkdtemp(prefix="ssa_oracle_")
+    try:
+        paths = {}
+        for name, a in arrays.items():
+            paths[name] = os.path.join(tmp, name + ".npy")
+            np.save(paths[name], np.ascontiguousarray(a))
+        nw = cpu_workers()
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(nw, initializer=_worker_init, initargs=(paths,)) as pool:
+            pool.map(_noop, range(4 * nw))
+            done = []
+            t0 = time.perf_counter()
+            for r in pool.imap_unordered(fn, tasks, chunksize=1):
+                done.append(r)
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            dt = time.perf_counter() - t0
+            pool.terminate()
+        return done, dt, nw
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+
+
+def cpu_baseline_prefill(cfg_id, lam, budget_s, np, synth, label):
+    """The oracle on the decision units of a prefill workload, in a seeded
+    random order (the whole workload if the budget allows)."""
     c = synth.CONFIGS[cfg_id]
     x = synth.prefill_inputs(cfg_id, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"],
                              frac=c["frac"])
     nQ = math.ceil(c["L"] / c["Br"])
-    rng = np.random.default_rng(1234)
-    units = [(0, int(h), int(i)) for h, i in zip(rng.integers(0, c["Hq"], 4096),
-                                                 rng.integers(0, nQ, 4096))]
-    done, flops = 0, 0.0
-    t0 = time.perf_counter()
-    for u in units:
-        oracle.prefill(x["q"], x["k"], x["v"], lam, c["Br"], c["Bc"], c["causal"], units=[u],
-                       bits=True)
-        i = u[2]
+    units = [(b, h, i) for b in range(c["B"]) for h in range(c["Hq"]) for i in range(nQ)]
+    order = np.random.default_rng(1234).permutation(len(units))
+    tasks = [(units[j], lam, c["Br"], c["Bc"], c["causal"]) for j in order]
+    done, dt, nw = run_cpu_pool({"q": x["q"], "k": x["k"], "v": x["v"]}, _prefill_unit_task, tasks, budget_s)
+    flops = 0.0
+    for (_, _, i) in done:
         r0, r1 = i * c["Br"], min(c["L"], (i + 1) * c["Br"])
         # dense-equivalent work of these rows: 4 d per allowed (row, key) pair
-        flops += 4.0 * c["d"] * sum(r + 1 for r in range(r0, r1))
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "dense-equiv TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{done} random query tiles (of {c['Hq'] * nQ}) of the 16K workload, "
-                      f"fp64 numpy, {dt:.1f} s"}
+        flops += 4.0 * c["d"] * (r1 * (r1 + 1) - r0 * (r0 + 1)) / 2
+    return {"value": flops / dt / 1e12, "unit": "dense-equiv TFLOP/s", "cores": nw, "kind": "oracle",
+            "sample": f"{len(done)} of {len(units)} query tiles (random order) of the {label} workload, "
+                      f"fp64 numpy, one process per core, {dt:.1f} s"}
+
+
+def cpu_baseline_decode(y, c, lam, budget_s, np):
+    """The oracle on (sequence, KV head) units of the decode workload;
+    tokens/s = finished units / Hkv per second."""
+    B, Hkv = c["B"], c["Hkv"]
+    units = [(b, h) for b in range(B) for h in range(Hkv)]
+    order = np.random.default_rng(1235).permutation(len(units))
+    tasks = [(units[j], lam, c["Bc"], c["split_tiles"]) for j in order]
+    arrays = {"q": y["q"], "k_cache": y["k_cache"], "v_cache": y["v_cache"], "seqlens": y["seqlens"]}
+    done, dt, nw = run_cpu_pool(arrays, _decode_unit_task, tasks, budget_s)
+    return {"value": len(done) / Hkv / dt, "unit": "tokens/s", "cores": nw, "kind": "oracle",
+            "sample": f"{len(done)} of {len(units)} (sequence, KV head) units (random order) of the "
+                      f"decode workload, fp64 numpy, one process per core, {dt:.1f} s"}
+
+
+def cpu_baseline_sparse(x, c, budget_s, np):
+    """The oracle's block mask and block-sparse prefill, one task per head."""
+    tasks = [(h, c["lam"], c["pool"], c["topk"], c["sink_blocks"], c["window_tokens"]) for h in range(c["Hq"])]
+    done, dt, nw = run_cpu_pool({"q": x["q"], "k": x["k"], "v": x["v"]}, _sparse_head_task, tasks, budget_s)
+    flops = 4.0 * c["d"] * c["L"] * (c["L"] + 1) / 2 * len(done)
+    return {"value": flops / dt / 1e12, "unit": "dense-equiv TFLOP/s", "cores": nw, "kind": "oracle",
+            "sample": f"{len(done)} of {c['Hq']} heads (mask + block-sparse prefill) of the 32K block-sparse "
+                      f"workload, fp64 numpy, one process per core, {dt:.1f} s"}
 
 
 def extra_128k(args, torch, np, ssa, synth):
@@ -169,16 +350,16 @@ def extra_128k(args, torch, np, ssa, synth):
     c = p["cfg"]
     rows = []
     for lam in c["lam_sweep"]:
-        state, ms, ev = run_prefill(p, lam, 3, 1, torch, ssa)
-        vis, kept, ex = prefill_work(state, c["Br"], c["Bc"], c["d"])
+        vis, kept, ms, ev = run_prefill(p, lam, 3, 1, torch, ssa, check_stats=False)
+        ex = 2.0 * c["Br"] * c["Bc"] * c["d"] * (vis + kept)
         rows.append({"lambda": lam, "ms": round(ms, 3), "dense_equiv_tflops": round(dense_flops(c) / ms / 1e9, 1),
                      "mfma_frac_executed": round(ex / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "skip_pct": round(100.0 * (vis - kept) / vis, 3)})
     # also at a calibrated ~50% point
     from sparse_attention_long_skip_amd.calibrate import calibrate_prefill
     lam50, _ = calibrate_prefill(p["q"], p["k"], p["v"], 0.5, c["Br"], c["Bc"], True)
-    state, ms, ev = run_prefill(p, lam50, 3, 1, torch, ssa)
-    vis, kept, ex = prefill_work(state, c["Br"], c["Bc"], c["d"])
+    vis, kept, ms, ev = run_prefill(p, lam50, 3, 1, torch, ssa, check_stats=False)
+    ex = 2.0 * c["Br"] * c["Bc"] * c["d"] * (vis + kept)
     rows.append({"lambda": round(lam50, 5), "label": "calibrated ~50% (extra point)", "ms": round(ms, 3),
                  "dense_equiv_tflops": round(dense_flops(c) / ms / 1e9, 1),
                  "mfma_frac_executed": round(ex / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -197,61 +378,73 @@ def extra_decode(args, torch, np, ssa, synth):
     vc = dev_bf16(y["v_cache"], torch, np)
     lens = y["seqlens"]
     seq = torch.from_numpy(lens.astype(np.int32)).cuda()
-    del y
-    T = c["split_tiles"]
-    lam, _ = calibrate_decode(q, kc, vc, seq, c["target_skip"], T, c["Bc"])
-    st = ssa.decode(q, kc, vc, seq, lam, split_tiles=T, stats=True)
+    T, Bc = c["split_tiles"], c["Bc"]
+    lam, _ = calibrate_decode(q, kc, vc, seq, c["target_skip"], T, Bc)
+    ws = torch.empty(ssa.decode_workspace_size(c["B"], c["Hq"], c["S_max"], c["d"], Bc, T),
+                     dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty((c["B"], c["Hq"]), dtype=torch.float32, device=q.device)
+    nS = math.ceil(math.ceil(c["S_max"] / Bc) / T)
+    counts = torch.empty((c["B"], c["Hkv"], nS), dtype=torch.int32, device=q.device)
+    fn = lambda: ssa.decode(q, kc, vc, seq, lam, split_tiles=T, workspace=ws, out=out, lse_out=lse,
+                            skip_counts=counts)
+    ms, ev = time_launches(fn, 20, 5, torch)
+    # kept V tiles from the timed launches' own skip counts, checked against
+    # a statistics launch
+    vis = c["Hkv"] * sum(math.ceil(int(n) / Bc) for n in lens)
+    kept = vis - int(counts.sum().item())
+    st = ssa.decode(q, kc, vc, seq, lam, split_tiles=T, stats=True, lse=False)
     torch.cuda.synchronize()
     state = st["tile_state"].cpu().numpy()
-    vis, kept = int((state != 0).sum()), int((state == 1).sum())
-    ws = st["workspace"]
-    out = torch.empty_like(q)
-    fn = lambda: ssa.decode(q, kc, vc, seq, lam, split_tiles=T, workspace=ws, out=out)
-    ms, ev = time_launches(fn, 20, 5, torch)
-    d, Hkv, Bc = c["d"], c["Hkv"], c["Bc"]
-    nS = math.ceil(math.ceil(c["S_max"] / Bc) / T)
-    k_bytes = 2.0 * d * Hkv * float(lens.sum())
-    v_bytes = 2.0 * d * Bc * kept
-    io = 2.0 * 2 * c["B"] * c["Hq"] * d
-    wsb = 2.0 * 4 * c["B"] * c["Hq"] * sum(math.ceil(math.ceil(n / Bc) / T) for n in lens) * (d + 2)
-    loaded = k_bytes + v_bytes + io + wsb
-    return {"workload": f"decode B=32 Hq=32 Hkv=8 d=128 lens U[16K,32K] split {T} tiles",
-            "lambda": round(lam, 5), "tokens_per_s": round(c["B"] / (ms * 1e-3), 1), "ms": round(ms, 4),
-            "event_ms": round(ev, 4), "skip_pct_v_tiles": round(100.0 * (vis - kept) / vis, 3),
-            "loaded_bytes": loaded, "hbm_gbs": round(loaded / (ev * 1e-3) / 1e9, 1),
-            "hbm_frac": round(loaded / (ev * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if (int((state != 0).sum()), int((state == 1).sum())) != (vis, kept):
+        raise RuntimeError("decode: timed launch counts differ from the statistics launch")
+    loaded = float(decode_loaded_bytes(lens, c["B"], c["Hq"], c["Hkv"], c["d"], Bc, T, kept))
+    res = {"workload": f"decode B=32 Hq=32 Hkv=8 d=128 lens U[16K,32K] split {T} tiles",
+           "lambda": round(lam, 5), "tokens_per_s": round(c["B"] / (ms * 1e-3), 1), "ms": round(ms, 4),
+           "event_ms": round(ev, 4), "skip_pct_v_tiles": round(100.0 * (vis - kept) / vis, 3),
+           "visited_tiles": vis, "kept_tiles": kept,
+           "loaded_bytes": loaded, "hbm_gbs": round(loaded / (ev * 1e-3) / 1e9, 1),
+           "hbm_frac": round(loaded / (ev * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del q, kc, vc, st
+    if not args.no_cpu:
+        log("cpu baseline: oracle on the decode workload")
+        try:
+            res["cpu_baseline"] = cpu_baseline_decode(y, c, lam, args.cpu_budget, np)
+        except Exception as e:  # report, keep the GPU figures
+            res["cpu_baseline"] = {"error": repr(e)}
+    return res
 
 
 def extra_sparse(args, torch, np, ssa, synth):
     c = synth.CONFIGS[4]
     x = synth.prefill_inputs(4, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"], frac=c["frac"])
     q, k, v = (dev_bf16(x[n], torch, np) for n in ("q", "k", "v"))
-    del x
     m = ssa.block_mask(q, k, c["pool"], c["topk"], c["sink_blocks"], c["window_tokens"])
     torch.cuda.synchronize()
     cnt = m["block_cnt"]
     nB = cnt.shape[-1]
     n_causal = c["Hq"] * nB * (nB + 1) / 2
-    st = ssa.prefill(q, k, v, c["lam"], Br=64, Bc=64, causal=True, block_idx=m["block_idx"],
-                     block_cnt=cnt, stats=True)
-    torch.cuda.synchronize()
-    state = st["tile_state"].cpu().numpy()
-    vis, kept = int((state != 0).sum()), int((state == 1).sum())
     ws = m["workspace"]
     fm = lambda: ssa.block_mask(q, k, c["pool"], c["topk"], c["sink_blocks"], c["window_tokens"], workspace=ws)
     ms_mask, ev_mask = time_launches(fm, 10, 3, torch)
-    out = torch.empty_like(q)
-    fp = lambda: ssa.prefill(q, k, v, c["lam"], Br=64, Bc=64, causal=True, block_idx=m["block_idx"],
-                             block_cnt=cnt, out=out)
-    ms_p, ev_p = time_launches(fp, 10, 3, torch)
+    kw = dict(Br=64, Bc=64, causal=True, block_idx=m["block_idx"], block_cnt=cnt)
+    vis, kept, ms_p, ev_p = time_prefill_legs(q, k, v, c["lam"], kw, 10, 3, torch, ssa)
     ex = 2.0 * 64 * 64 * c["d"] * (vis + kept)
-    return {"workload": "block-sparse prefill 32K H=16 d=64, pooled top-64 + sink + 1024 window, lambda=-6",
+    res = {"workload": "block-sparse prefill 32K H=16 d=64, pooled top-64 + sink + 1024 window, lambda=-6",
             "mask_ms": round(ms_mask, 4), "mask_hbm_gbs": round(2 * 2 * c["Hq"] * c["L"] * c["d"] / (ev_mask * 1e-3) / 1e9, 1),
             "prefill_ms": round(ms_p, 4), "mask_density": round(vis / n_causal, 4),
             "in_mask_skip_pct": round(100.0 * (vis - kept) / vis, 3),
             "combined_sparsity": round(1 - kept / n_causal, 4),
             "dense_equiv_tflops": round(dense_flops(c) / (ms_mask + ms_p) / 1e9, 1),
             "mfma_frac_executed": round(ex / (ev_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del q, k, v, m
+    if not args.no_cpu:
+        log("cpu baseline: oracle on the block-sparse workload")
+        try:
+            res["cpu_baseline"] = cpu_baseline_sparse(x, c, args.cpu_budget, np)
+        except Exception as e:  # report, keep the GPU figures
+            res["cpu_baseline"] = {"error": repr(e)}
+    return res
 
 
 def extra_sparge(args, torch, np, ssa, synth):
@@ -269,15 +462,10 @@ def extra_sparge(args, torch, np, ssa, synth):
     nB = cnt.shape[-1]
     n_causal = c["Hq"] * nB * (nB + 1) / 2
     kw = dict(Br=64, Bc=64, causal=True, block_idx=m["block_idx"], block_cnt=cnt)
-    st = ssa.prefill(q, k, v, c["lam"], stats=True, **kw)
-    torch.cuda.synchronize()
-    state = st["tile_state"].cpu().numpy()
-    vis, kept = int((state != 0).sum()), int((state == 1).sum())
     ws = m["workspace"]
     fm = lambda: ssa.sparge_mask(q, k, c["theta"], c["tau"], "mass", c["pool"], workspace=ws)
     ms_mask, ev_mask = time_launches(fm, 10, 3, torch)
-    out = torch.empty_like(q)
-    ms_p, ev_p = time_launches(lambda: ssa.prefill(q, k, v, c["lam"], out=out, **kw), 10, 3, torch)
+    vis, kept, ms_p, ev_p = time_prefill_legs(q, k, v, c["lam"], kw, 10, 3, torch, ssa)
     ex = 2.0 * 64 * 64 * c["d"] * (vis + kept)
     return {"workload": "SpargeAttn two-stage prefill 32K H=16 d=64, drifting blocks, "
                         f"theta={c['theta']} tau={c['tau']} (P_hat mass), lambda={c['lam']}",
@@ -305,15 +493,10 @@ def extra_vslash(args, torch, np, ssa, synth):
     nB = cnt.shape[-1]
     n_causal = c["Hq"] * nB * (nB + 1) / 2
     kw = dict(Br=64, Bc=64, causal=True, block_idx=m["block_idx"], block_cnt=cnt)
-    st = ssa.prefill(q, k, v, c["lam"], stats=True, **kw)
-    torch.cuda.synchronize()
-    state = st["tile_state"].cpu().numpy()
-    vis, kept = int((state != 0).sum()), int((state == 1).sum())
     ws = m["workspace"]
     ms_mask, ev_mask = time_launches(lambda: ssa.vertical_slash_mask(q, k, nv, ns, R, workspace=ws),
                                      10, 3, torch)
-    out = torch.empty_like(q)
-    ms_p, ev_p = time_launches(lambda: ssa.prefill(q, k, v, c["lam"], out=out, **kw), 10, 3, torch)
+    vis, kept, ms_p, ev_p = time_prefill_legs(q, k, v, c["lam"], kw, 10, 3, torch, ssa)
     ex = 2.0 * 64 * 64 * c["d"] * (vis + kept)
     return {"workload": f"vertical-slash estimator 32K H=16 d=64 (last {R} queries, {nv} vertical, "
                         f"{ns} slash) + block-sparse prefill over its tiles, lambda={c['lam']}",
@@ -336,13 +519,8 @@ def extra_nm(args, torch, np, ssa, synth):
     kw = dict(Br=c["Br"], Bc=c["Bc"], causal=True, nm=(2, 4), dense_sink=64, dense_recent=256)
     m = ssa.prefill(q, k, v, -math.inf, margins=True, lse=False, **kw)["tile_margin"].cpu().numpy()
     rows = []
-    out = torch.empty_like(q)
     for lam in (-math.inf, lambda_for_ratio(m, 0.5)):
-        st = ssa.prefill(q, k, v, lam, stats=True, **kw)
-        torch.cuda.synchronize()
-        s = st["tile_state"].cpu().numpy()
-        vis, kept = int((s != 0).sum()), int((s == 1).sum())
-        ms, ev = time_launches(lambda: ssa.prefill(q, k, v, lam, out=out, **kw), 10, 3, torch)
+        vis, kept, ms, ev = time_prefill_legs(q, k, v, lam, kw, 10, 3, torch, ssa)
         rows.append({"lambda": None if lam == -math.inf else round(lam, 5), "ms": round(ms, 4),
                      "skip_pct": round(100.0 * (vis - kept) / vis, 3),
                      "dense_equiv_tflops": round(dense_flops(c) / ms / 1e9, 1),
@@ -387,7 +565,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="wall seconds per CPU-baseline leg (the oracle in worker processes)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baselines")
     ap.add_argument("--only-main", action="store_true", help="skip extra and cpu baseline (profiling)")
     ap.add_argument("--leg", choices=["prefill_128k", "decode", "block_sparse_32k", "sparge_32k",
                                       "vslash_32k", "nm_2of4_16k", "warp_units_16k"],
@@ -419,8 +599,8 @@ def main():
     p = bench_prefill(1, args, torch, np, ssa, synth, target=c["target_skip"])
     lam = p["lam"]
     log(f"lambda {lam:.5f} (calibrated ratio {p['calibrated_ratio']:.4f}); timing {args.steps} steps")
-    state, ms, ev_ms = run_prefill(p, lam, args.steps, args.warmup, torch, ssa)
-    vis, kept, ex = prefill_work(state, c["Br"], c["Bc"], c["d"])
+    vis, kept, ms, ev_ms = run_prefill(p, lam, args.steps, args.warmup, torch, ssa)
+    ex = 2.0 * c["Br"] * c["Bc"] * c["d"] * (vis + kept)
     dense = dense_flops(c)
     value = dense / (ms * 1e-3) / 1e12
     achieved = ex / (ev_ms * 1e-3) / 1e12
@@ -471,9 +651,9 @@ def main():
                 extra[name] = {"error": repr(e)}
             torch.cuda.empty_cache()
         result["extra"] = extra
-    if not args.only_main:
-        log("cpu baseline: oracle on a sample of the 16K workload")
-        result["cpu_baseline"] = cpu_baseline_prefill(1, lam, args.cpu_budget, np, synth)
+    if not (args.only_main or args.no_cpu):
+        log("cpu baseline: oracle on the 16K workload")
+        result["cpu_baseline"] = cpu_baseline_prefill(1, lam, args.cpu_budget, np, synth, "16K")
     print(json.dumps(result), flush=True)
 
 

@@ -122,11 +122,16 @@ def _check(fn, status):
 def prefill(q, k, v, lam: float, Br: int = 128, Bc: int = 64, causal: bool = True,
             block_idx=None, block_cnt=None, lse: bool = True, stats: bool = False,
             margins: bool = False, out=None, stream=None, nm=None, dense_sink: int = 0,
-            dense_recent: int = 0) -> dict:
+            dense_recent: int = 0, counts: bool = False, skip_counts=None, lse_out=None) -> dict:
     """Skip-Softmax prefill (``ssa_prefill``; ``ssa_prefill_nm`` when ``nm`` =
     (N, M) asks for N:M sparse softmax). q [B,Hq,L,d], k/v [B,Hkv,L,d] bf16.
     Returns a dict: out, and lse / skip_counts / tile_state / tile_margin as
-    requested (tile arrays are zero / NaN where not visited)."""
+    requested (tile arrays are zero / NaN where not visited).
+
+    ``stats`` asks for skip_counts and tile_state, ``margins`` for
+    tile_margin; either selects the kernel instance that writes per-tile
+    arrays. ``counts`` (or a caller-provided ``skip_counts`` tensor) asks for
+    skip_counts alone, which the plain instance writes as well."""
     _need(q, "q", torch.bfloat16, 4)
     _need(k, "k", torch.bfloat16, 4)
     _need(v, "v", torch.bfloat16, 4)
@@ -136,8 +141,19 @@ def prefill(q, k, v, lam: float, Br: int = 128, Bc: int = 64, causal: bool = Tru
     dev = q.device
     res = {}
     res["out"] = out if out is not None else torch.empty_like(q)
-    res["lse"] = torch.empty((B, Hq, L), dtype=torch.float32, device=dev) if lse else None
-    res["skip_counts"] = torch.empty((B, Hq, nQ), dtype=torch.int32, device=dev) if stats else None
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, 3)
+        res["lse"] = lse_out
+    else:
+        res["lse"] = torch.empty((B, Hq, L), dtype=torch.float32, device=dev) if lse else None
+    if skip_counts is not None:
+        _need(skip_counts, "skip_counts", torch.int32, 3)
+        if tuple(skip_counts.shape) != (B, Hq, nQ):
+            raise ValueError(f"skip_counts must be {(B, Hq, nQ)}, got {tuple(skip_counts.shape)}")
+        res["skip_counts"] = skip_counts
+    else:
+        res["skip_counts"] = (torch.empty((B, Hq, nQ), dtype=torch.int32, device=dev)
+                              if (stats or counts) else None)
     res["tile_state"] = torch.zeros((B, Hq, nQ, nK), dtype=torch.uint8, device=dev) if stats else None
     res["tile_margin"] = (torch.full((B, Hq, nQ, nK), float("nan"), dtype=torch.float32, device=dev)
                           if margins else None)
@@ -170,9 +186,11 @@ def decode_workspace_size(B, Hq, S_max, d, Bc=64, split_tiles=32) -> int:
 
 def decode(q, k_cache, v_cache, seqlens, lam: float, split_tiles: int = 32, Bc: int = 64,
            workspace=None, lse: bool = True, stats: bool = False, margins: bool = False,
-           out=None, stream=None) -> dict:
+           out=None, stream=None, lse_out=None, skip_counts=None, counts: bool = False) -> dict:
     """Skip-Softmax split-K decode (``ssa_decode``). q [B,Hq,d]; caches
-    [B,Hkv,S_max,d] bf16; seqlens [B] int32 (device)."""
+    [B,Hkv,S_max,d] bf16; seqlens [B] int32 (device). ``stats`` asks for
+    skip_counts and tile_state, ``counts`` for skip_counts alone; ``lse_out``
+    and ``skip_counts`` may be caller-provided tensors."""
     _need(q, "q", torch.bfloat16, 3)
     _need(k_cache, "k_cache", torch.bfloat16, 4)
     _need(v_cache, "v_cache", torch.bfloat16, 4)
@@ -187,8 +205,19 @@ def decode(q, k_cache, v_cache, seqlens, lam: float, split_tiles: int = 32, Bc: 
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     res = {"workspace": workspace}
     res["out"] = out if out is not None else torch.empty_like(q)
-    res["lse"] = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse else None
-    res["skip_counts"] = torch.empty((B, Hkv, nS), dtype=torch.int32, device=dev) if stats else None
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, 2)
+        res["lse"] = lse_out
+    else:
+        res["lse"] = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse else None
+    if skip_counts is not None:
+        _need(skip_counts, "skip_counts", torch.int32, 3)
+        if tuple(skip_counts.shape) != (B, Hkv, nS):
+            raise ValueError(f"skip_counts must be {(B, Hkv, nS)}, got {tuple(skip_counts.shape)}")
+        res["skip_counts"] = skip_counts
+    else:
+        res["skip_counts"] = (torch.empty((B, Hkv, nS), dtype=torch.int32, device=dev)
+                              if (stats or counts) else None)
     res["tile_state"] = torch.zeros((B, Hkv, nT), dtype=torch.uint8, device=dev) if stats else None
     res["tile_margin"] = (torch.full((B, Hkv, nT), float("nan"), dtype=torch.float32, device=dev)
                           if margins else None)

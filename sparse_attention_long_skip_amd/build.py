@@ -32,6 +32,9 @@ def build(verbose: bool = False, jobs: int = 4, lib_path: str = LIB, overrides: 
     (libssa.so in the package by default). ``overrides`` maps a source name
     to another file to compile in its place. Always rebuilds. Returns the
     library path."""
+    if not lib_path or os.path.isdir(lib_path):
+        raise ValueError(f"lib_path must name the library file to write, got {lib_path!r}")
+    lib_path = os.path.abspath(lib_path)
     overrides = overrides or {}
     objdir = objdir or os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)

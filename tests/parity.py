@@ -71,18 +71,30 @@ def compare_decisions(gpu_state, ref_decision, ref_margin, lam, band=BAND):
 
 
 def prefill_parity(q_bits, k_bits, v_bits, lam, Br, Bc, causal, block_idx=None, block_cnt=None,
-                   units=None, margins_atol=1e-3, nm=None, dense_sink=0, dense_recent=0):
+                   units=None, margins_atol=1e-3, nm=None, dense_sink=0, dense_recent=0,
+                   dev_block=None):
     """Run the HIP prefill on the whole input and the oracle on ``units``
-    (all if None); compare. Returns a summary dict."""
+    (all if None); compare. Returns a summary dict.
+
+    Two kernel instances run on the same input: the statistics instance
+    (per-tile decisions and margins, compared tile by tile) and the plain
+    instance that the benchmark times (out, lse and per-unit skip counts
+    only). Both must match the oracle; their skip counts must be equal.
+    ``dev_block`` = (block_idx, block_cnt) device tensors feeds both kernels
+    a list built on the GPU (the oracle then takes the host copy given as
+    ``block_idx`` / ``block_cnt``)."""
     import sparse_attention_long_skip_amd as ssa
     q, k, v = dev_bf16(q_bits), dev_bf16(k_bits), dev_bf16(v_bits)
     bi = bc = None
-    if block_idx is not None:
+    if dev_block is not None:
+        bi, bc = dev_block
+    elif block_idx is not None:
         bi = torch.from_numpy(np.ascontiguousarray(block_idx, np.int32)).cuda()
         bc = torch.from_numpy(np.ascontiguousarray(block_cnt, np.int32)).cuda()
-    g = ssa.prefill(q, k, v, lam, Br=Br, Bc=Bc, causal=causal, block_idx=bi, block_cnt=bc,
-                    lse=True, stats=True, margins=True, nm=nm, dense_sink=dense_sink,
-                    dense_recent=dense_recent)
+    kw = dict(Br=Br, Bc=Bc, causal=causal, block_idx=bi, block_cnt=bc, lse=True, nm=nm,
+              dense_sink=dense_sink, dense_recent=dense_recent)
+    g = ssa.prefill(q, k, v, lam, stats=True, margins=True, **kw)
+    gp = ssa.prefill(q, k, v, lam, counts=True, **kw)
     torch.cuda.synchronize()
     ref = oracle.prefill(q_bits, k_bits, v_bits, lam, Br, Bc, causal, block_idx=block_idx,
                          block_cnt=block_cnt, units=units, bits=True, nm=nm,
@@ -102,12 +114,21 @@ def prefill_parity(q_bits, k_bits, v_bits, lam, Br, Bc, causal, block_idx=None, 
     fin = vis & np.isfinite(rm)
     if fin.any():
         assert np.max(np.abs(gm[fin] - rm[fin])) < margins_atol
-    # skip counts
+    # skip counts: the statistics instance's agree with its tile decisions,
+    # the plain instance's with the statistics instance's (same fp32 scores,
+    # same rule), and both with the oracle's wherever no decision of the
+    # unit lies in the band
     sc = to_np(g["skip_counts"])[sel]
     assert np.array_equal(sc, (state[sel] == SKIPPED).sum(axis=-1))
-    # outputs, unit by unit rows
+    sc_plain = to_np(gp["skip_counts"])[sel]
+    assert np.array_equal(sc_plain, sc), "plain instance skip counts differ from the tile decisions"
+    clean = ~diff.any(axis=-1)
+    assert np.array_equal(sc_plain[clean], ref["skip_counts"][sel][clean])
+    # outputs, unit by unit rows, for both instances
     out_g = to_np(g["out"])
     lse_g = to_np(g["lse"])
+    out_p = to_np(gp["out"])
+    lse_p = to_np(gp["lse"])
     replay_units = [u for u, dd in zip(units, diff.any(axis=-1)) if dd]
     rep = None
     if replay_units:
@@ -115,7 +136,7 @@ def prefill_parity(q_bits, k_bits, v_bits, lam, Br, Bc, causal, block_idx=None, 
         rep = oracle.replay(q_bits, k_bits, v_bits, forced, Br, Bc, causal, block_idx=block_idx,
                             block_cnt=block_cnt, units=replay_units, bits=True, nm=nm,
                             dense_sink=dense_sink, dense_recent=dense_recent)
-    got_o, ref_o, got_l, ref_l = [], [], [], []
+    got_o, ref_o, got_l, ref_l, pl_o, pl_l = [], [], [], [], [], []
     rs = set(replay_units)
     for (b, h, i) in units:
         r0, r1 = i * Br, min(L, (i + 1) * Br)
@@ -124,12 +145,19 @@ def prefill_parity(q_bits, k_bits, v_bits, lam, Br, Bc, causal, block_idx=None, 
         ref_o.append(src["out"][b, h, r0:r1])
         got_l.append(lse_g[b, h, r0:r1])
         ref_l.append(src["lse"][b, h, r0:r1])
-    mo = assert_close("out", np.concatenate(got_o), np.concatenate(ref_o))
-    ml = assert_close("lse", np.concatenate(got_l), np.concatenate(ref_l), rtol_l2=1.0)
+        pl_o.append(out_p[b, h, r0:r1])
+        pl_l.append(lse_p[b, h, r0:r1])
+    ref_o, ref_l = np.concatenate(ref_o), np.concatenate(ref_l)
+    mo = assert_close("out", np.concatenate(got_o), ref_o)
+    ml = assert_close("lse", np.concatenate(got_l), ref_l, rtol_l2=1.0)
+    mp = assert_close("out (plain instance)", np.concatenate(pl_o), ref_o)
+    assert_close("lse (plain instance)", np.concatenate(pl_l), ref_l, rtol_l2=1.0)
+    same = bool(np.array_equal(out_p, out_g) and np.array_equal(lse_p, lse_g, equal_nan=True))
     n_vis = int(vis.sum())
     n_skip = int((state[sel] == SKIPPED).sum())
     return {"max_err_out": mo[0], "rel_l2_out": mo[1], "max_err_lse": ml[0], "exempt": n_exempt,
-            "visited": n_vis, "skipped": n_skip, "gpu": g, "ref": ref}
+            "visited": n_vis, "skipped": n_skip, "gpu": g, "gpu_plain": gp, "ref": ref,
+            "max_err_out_plain": mp[0], "plain_bit_identical": same}
 
 
 def decode_parity(y, lam, T, units=None, Bc=64):

@@ -80,16 +80,78 @@ def test_config2_decode_half_v_tiles_skipped():
     assert 0.3 < r["skipped"] / r["visited"] < 0.7
 
 
-def test_config4_mask_and_block_sparse_prefill():
+def test_config3_128k_calibrated_half_skipped():
+    # the calibrated ~50% point that the benchmark also reports for 128K
+    c = synth.CONFIGS[3]
+    x = synth.prefill_inputs(3, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"], frac=c["frac"])
+    nQ = math.ceil(c["L"] / c["Br"])
+    units = _units(np.random.default_rng(15), c["B"], c["Hq"], nQ, 5)
+    m = oracle.prefill(x["q"], x["k"], x["v"], -math.inf, c["Br"], c["Bc"], True, units=units, bits=True)["margin"]
+    lam = oracle.lambda_for_ratio(m, 0.5)
+    r = prefill_parity(x["q"], x["k"], x["v"], lam, c["Br"], c["Bc"], True, units=units)
+    print(f"config 3 calibrated: lambda {lam:.4f}, sampled skip {r['skipped']}/{r['visited']}, "
+          f"exempt {r['exempt']}, max err {r['max_err_out']:.2e}")
+    assert 0.3 < r["skipped"] / r["visited"] < 0.7
+
+
+def test_config4_chain_gpu_mask_then_gpu_prefill():
+    """The benchmarked chain end to end: the GPU block mask (all 16 heads
+    against the oracle's mask) feeds both prefill instances on the device;
+    the oracle prefill runs over the oracle's mask, except in rows where the
+    two masks differ at a near-tie (then over the GPU's row)."""
     c = synth.CONFIGS[4]
     x = synth.prefill_inputs(4, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"], frac=c["frac"])
-    mk = mask_parity(x["q"], x["k"], c["pool"], c["topk"], c["sink_blocks"], c["window_tokens"],
-                     heads=[(0, 0), (0, 9)])
-    print(f"config 4 mask: near-tie differences {mk['ties']}")
-    ref = oracle.block_mask(x["q"], x["k"], c["pool"], c["topk"], c["sink_blocks"], c["window_tokens"], bits=True)
+    mk = mask_parity(x["q"], x["k"], c["pool"], c["topk"], c["sink_blocks"], c["window_tokens"])
+    g = mk["gpu"]
+    gi = g["block_idx"].cpu().numpy()
+    gc = g["block_cnt"].cpu().numpy()
+    host_idx = np.stack([mk["refs"][(0, h)]["block_idx"][0, 0] for h in range(c["Hq"])])[None].astype(np.int32)
+    host_cnt = np.stack([mk["refs"][(0, h)]["block_cnt"][0, 0] for h in range(c["Hq"])])[None].astype(np.int32)
+    differ = np.any(gi != host_idx, axis=-1) | (gc != host_cnt)
+    host_idx[differ] = gi[differ]
+    host_cnt[differ] = gc[differ]
+    print(f"config 4 mask: {mk['ties']} near-tie differences in {int(differ.sum())} rows")
     nQ = math.ceil(c["L"] / c["Br"])
     units = _units(np.random.default_rng(14), c["B"], c["Hq"], nQ, 10)
+    units = sorted(set(units) | {(0, int(h), int(i)) for h, i in np.argwhere(differ[0])[:4]})
     r = prefill_parity(x["q"], x["k"], x["v"], c["lam"], c["Br"], c["Bc"], True,
-                       block_idx=ref["block_idx"].astype(np.int32), block_cnt=ref["block_cnt"].astype(np.int32),
-                       units=units)
-    print(f"config 4 prefill: sampled skip {r['skipped']}/{r['visited']}, max err {r['max_err_out']:.2e}")
+                       block_idx=host_idx, block_cnt=host_cnt, units=units,
+                       dev_block=(g["block_idx"], g["block_cnt"]))
+    print(f"config 4 prefill: sampled skip {r['skipped']}/{r['visited']}, max err {r['max_err_out']:.2e}, "
+          f"plain instance bit-identical to stats instance: {r['plain_bit_identical']}")
+
+
+def test_sparge_32k_chain_gpu_lists():
+    """The SpargeAttn leg as benchmarked: stage one on the GPU (its lists
+    checked against the oracle's stage one on sampled heads), stage two in
+    both prefill instances over the device lists, sampled units against the
+    oracle over the same lists."""
+    from parity import sparge_parity
+    c = synth.SPARGE
+    x = synth.prefill_inputs(c["cfg_id"], 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"],
+                             frac=c["frac"], drift=c["drift"])
+    sp = sparge_parity(x["q"], x["k"], c["theta"], c["tau"], "mass", c["pool"], heads=[(0, 2), (0, 13)])
+    g = sp["gpu"]
+    nQ = math.ceil(c["L"] / c["Br"])
+    units = _units(np.random.default_rng(16), c["B"], c["Hq"], nQ, 8)
+    r = prefill_parity(x["q"], x["k"], x["v"], c["lam"], c["Br"], c["Bc"], True,
+                       block_idx=g["block_idx"].cpu().numpy(), block_cnt=g["block_cnt"].cpu().numpy(),
+                       units=units, dev_block=(g["block_idx"], g["block_cnt"]))
+    print(f"sparge 32K: near rows {sp['near']}, sampled skip {r['skipped']}/{r['visited']}, "
+          f"max err {r['max_err_out']:.2e}")
+
+
+def test_vslash_32k_chain_gpu_lists():
+    """The vertical-slash leg as benchmarked (last 64 queries, 1000 vertical
+    keys, 64 slash offsets), its tile lists feeding both prefill instances."""
+    from parity import vslash_parity
+    c = synth.CONFIGS[4]
+    x = synth.prefill_inputs(4, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"], frac=c["frac"])
+    vs = vslash_parity(x["q"], x["k"], 64, 1000, 64, heads=[(0, 5)])
+    g = vs["gpu"]
+    nQ = math.ceil(c["L"] / c["Br"])
+    units = _units(np.random.default_rng(17), c["B"], c["Hq"], nQ, 8)
+    r = prefill_parity(x["q"], x["k"], x["v"], c["lam"], c["Br"], c["Bc"], True,
+                       block_idx=g["block_idx"].cpu().numpy(), block_cnt=g["block_cnt"].cpu().numpy(),
+                       units=units, dev_block=(g["block_idx"], g["block_cnt"]))
+    print(f"vertical-slash 32K: sampled skip {r['skipped']}/{r['visited']}, max err {r['max_err_out']:.2e}")

@@ -36,8 +36,9 @@ def test_skip_small_gqa(d, Br):
     r = prefill_parity(q, k, v, lam, Br, 64, True)
     print(f"lam={lam:.4f} skipped {r['skipped']}/{r['visited']} exempt {r['exempt']} "
           f"err {r['max_err_out']:.2e}")
-    # at this length half the margins are positive, so lambda clamps to 0;
-    # a fifth of the tiles still skip
+    # at this length more than half of the margins are positive (the running
+    # max is still growing), so lambda clamps to 0 and fewer tiles skip than
+    # asked for: about 20% with 64-row units, 6-7% with 128-row units
     assert r["skipped"] > 0.05 * r["visited"]
 
 
