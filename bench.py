@@ -150,6 +150,26 @@ def bench_prefill(cfg_id, args, torch, np, ssa, synth, lam=None, target=None, se
     return res
 
 
+def time_calibration(p, target, torch, ssa):
+    """Device threshold calibration of a prefill workload: the dense
+    statistics launch that writes the tile margins, and the quantile over
+    them (``ssa_lambda_for_ratio``), timed separately."""
+    c = p["cfg"]
+    q, k, v = p["q"], p["k"], p["v"]
+    B, Hq, L, d = q.shape
+    out = torch.empty_like(q)
+    kw = dict(Br=c["Br"], Bc=c["Bc"], causal=c["causal"], lse=False, out=out)
+    ms_m, ev_m = time_launches(lambda: ssa.prefill(q, k, v, -math.inf, margins=True, **kw), 3, 1, torch)
+    mm = ssa.prefill(q, k, v, -math.inf, margins=True, **kw)["tile_margin"]
+    ws = torch.empty(ssa.calibrate_workspace_size(mm.numel()), dtype=torch.uint8, device=q.device)
+    r = torch.empty(4, dtype=torch.float64, device=q.device)
+    ms_q, ev_q = time_launches(lambda: ssa.lambda_for_ratio(mm, target, workspace=ws, result=r, sync=False),
+                               10, 3, torch)
+    return {"margins": int(mm.numel()), "visited": int(r[2].item()), "lambda": float(r[0].item()),
+            "ratio": round(float(r[1].item()), 5), "margin_launch_ms": round(ev_m, 4),
+            "quantile_ms": round(ms_q, 4), "quantile_event_ms": round(ev_q, 4)}
+
+
 def run_prefill(p, lam, steps, warmup, torch, ssa, check_stats=True):
     """Time the plain prefill instance (out, lse and per-unit skip counts).
     The kept-tile count comes from the skip counts of the last timed launch;
@@ -356,8 +376,8 @@ def extra_128k(args, torch, np, ssa, synth):
                      "mfma_frac_executed": round(ex / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                      "skip_pct": round(100.0 * (vis - kept) / vis, 3)})
     # also at a calibrated ~50% point
-    from sparse_attention_long_skip_amd.calibrate import calibrate_prefill
-    lam50, _ = calibrate_prefill(p["q"], p["k"], p["v"], 0.5, c["Br"], c["Bc"], True)
+    cal = time_calibration(p, 0.5, torch, ssa)
+    lam50 = cal["lambda"]
     vis, kept, ms, ev = run_prefill(p, lam50, 3, 1, torch, ssa, check_stats=False)
     ex = 2.0 * c["Br"] * c["Bc"] * c["d"] * (vis + kept)
     rows.append({"lambda": round(lam50, 5), "label": "calibrated ~50% (extra point)", "ms": round(ms, 3),
@@ -365,7 +385,8 @@ def extra_128k(args, torch, np, ssa, synth):
                  "mfma_frac_executed": round(ex / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                  "skip_pct": round(100.0 * (vis - kept) / vis, 3)})
     del p
-    return {"workload": "prefill 128K B=1 Hq=8 Hkv=1 d=128 causal Br=128 Bc=64, 5% planted", "sweep": rows}
+    return {"workload": "prefill 128K B=1 Hq=8 Hkv=1 d=128 causal Br=128 Bc=64, 5% planted", "sweep": rows,
+            "calibration": cal}
 
 
 def extra_decode(args, torch, np, ssa, synth):
@@ -511,15 +532,15 @@ def extra_vslash(args, torch, np, ssa, synth):
 
 def extra_nm(args, torch, np, ssa, synth):
     """N:M (2:4) sparse softmax on the 16K GQA shape, alone and with ~50% tile skipping."""
-    from sparse_attention_long_skip_amd.calibrate import lambda_for_ratio
+    from sparse_attention_long_skip_amd.calibrate import calibrate_prefill
     c = synth.CONFIGS[1]
     x = synth.prefill_inputs(1, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"], frac=c["frac"])
     q, k, v = (dev_bf16(x[n], torch, np) for n in ("q", "k", "v"))
     del x
     kw = dict(Br=c["Br"], Bc=c["Bc"], causal=True, nm=(2, 4), dense_sink=64, dense_recent=256)
-    m = ssa.prefill(q, k, v, -math.inf, margins=True, lse=False, **kw)["tile_margin"].cpu().numpy()
+    lam50, _ = calibrate_prefill(q, k, v, 0.5, **kw)
     rows = []
-    for lam in (-math.inf, lambda_for_ratio(m, 0.5)):
+    for lam in (-math.inf, lam50):
         vis, kept, ms, ev = time_prefill_legs(q, k, v, lam, kw, 10, 3, torch, ssa)
         rows.append({"lambda": None if lam == -math.inf else round(lam, 5), "ms": round(ms, 4),
                      "skip_pct": round(100.0 * (vis - kept) / vis, 3),
@@ -531,14 +552,13 @@ def extra_nm(args, torch, np, ssa, synth):
 def extra_warp_units(args, torch, np, ssa, synth):
     """Br = 32 decision units (the per-warp variant) on the 16K GQA shape,
     lambda calibrated to ~50% of the 32-row units' tiles skipped."""
-    from sparse_attention_long_skip_amd.calibrate import lambda_for_ratio
+    from sparse_attention_long_skip_amd.calibrate import calibrate_prefill
     c = synth.CONFIGS[1]
     x = synth.prefill_inputs(1, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"], frac=c["frac"])
     q, k, v = (dev_bf16(x[n], torch, np) for n in ("q", "k", "v"))
     del x
     kw = dict(Br=32, Bc=c["Bc"], causal=True)
-    m = ssa.prefill(q, k, v, -math.inf, margins=True, lse=False, **kw)["tile_margin"].cpu().numpy()
-    lam = lambda_for_ratio(m, 0.5)
+    lam, _ = calibrate_prefill(q, k, v, 0.5, **kw)
     st = ssa.prefill(q, k, v, lam, stats=True, **kw)
     torch.cuda.synchronize()
     s = st["tile_state"].cpu().numpy()  # [B, Hq, L / 32, nK]
@@ -631,6 +651,8 @@ def main():
                      "kernel": "prefill_kernel<128, 128, false, false, false, 4>", "kernel_ms": round(ev_ms, 4),
                      "executed_flops": ex},
     }
+    if not args.only_main:
+        result["config"]["calibration"] = time_calibration(p, c["target_skip"], torch, ssa)
     del p
     torch.cuda.empty_cache()
     if args.copy_probe:

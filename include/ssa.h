@@ -322,6 +322,48 @@ int ssa_vertical_slash_mask(const void* q, const void* k, int B, int H, int L, i
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ssa_calibrate_workspace_size -- bytes of device workspace that
+ * ssa_lambda_for_ratio needs for n_margins margins and the given rank
+ * window. Returns 0 for n_margins > 2^40 or window outside [0, 0.5].
+ */
+size_t ssa_calibrate_workspace_size(size_t n_margins, double window);
+
+/*
+ * ssa_lambda_for_ratio -- the threshold that skips a target share of the
+ * visited tiles, computed on the device from per-tile margins (TRT-LLM
+ * Skip Softmax page, efficiency and accuracy: an automatic calibration
+ * program finds the threshold for a target sparsity; Model Optimizer
+ * tutorial, step 4: calibrate the threshold to a target sparsity ratio).
+ *
+ * A tile's margin does not depend on lambda, so the skip set at lambda is
+ * {margin < lambda}. With g the sorted non-NaN margins (n of them; NaN marks
+ * a tile that was not visited), want = round-half-even(target * n),
+ * lo = max(1, floor((target - window) * n)), hi = min(n - 1,
+ * ceil((target + window) * n)), then lo = min(lo, max(1, want)) and
+ * hi = max(hi, min(n - 1, want)) (all in fp64): among the pairs
+ * (g[r-1], g[r]), lo <= r <= hi, with both values finite, the first one with
+ * the largest difference g[r] - g[r-1] gives lambda = (g[r-1] + g[r]) / 2;
+ * with no such pair, lambda = g[min(max(want, 0), n - 1)] if finite, else 0;
+ * n < 2 gives 0. Finally lambda = min(lambda, 0). Differences and the
+ * midpoint are taken in fp64 of the fp32 margins.
+ *
+ *  margins  device fp32 array of n_margins values (for instance the
+ *           tile_margin output of ssa_prefill or ssa_decode, initialised to
+ *           NaN); nullable only when n_margins = 0; 4-byte aligned.
+ *  target   in [0, 1]; window in [0, 0.5] (the rule above uses 0.01).
+ *  result   device array of 4 doubles, 8-byte aligned, written on the
+ *           stream: lambda, the achieved ratio (margins below lambda / n, 0
+ *           when n = 0), n, and the count of margins below lambda. lambda is
+ *           NaN only if the workspace bound was exceeded (not expected).
+ *  workspace at least ssa_calibrate_workspace_size(n_margins, window) bytes,
+ *           256-byte aligned; contents on entry are ignored.
+ *  Errors: SSA_ERR_INVALID_ARG (null pointers, target / window out of range,
+ *  misalignment), SSA_ERR_WORKSPACE.
+ */
+int ssa_lambda_for_ratio(const float* margins, size_t n_margins, double target, double window,
+                         double* result, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * ssa_lambda_from_scale_factor -- threshold from a context-length scale
  * factor (TRT-LLM page: the configured threshold_scale_factor is divided by
  * the context length to give the actual threshold, so longer contexts skip

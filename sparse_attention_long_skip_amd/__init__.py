@@ -15,5 +15,6 @@ from ._lib import (  # noqa: F401
     lambda_from_scale_factor, prefill, decode, decode_workspace_size, block_mask,
     block_mask_compressed_workspace_size,
     block_mask_max_blocks, block_mask_workspace_size, sparge_mask, sparge_mask_workspace_size,
-    TAU_MODES, vertical_slash_mask, vertical_slash_workspace_size,
+    TAU_MODES, vertical_slash_mask, vertical_slash_workspace_size, lambda_for_ratio,
+    calibrate_workspace_size,
 )

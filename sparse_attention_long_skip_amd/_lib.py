@@ -50,6 +50,8 @@ _SIGNATURES = {
     "ssa_vertical_slash_workspace_size": (_sz, [_i, _i, _i]),
     "ssa_vertical_slash_mask": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p,
                                      _p, _p, _p, _sz, _p]),
+    "ssa_calibrate_workspace_size": (_sz, [_sz, ctypes.c_double]),
+    "ssa_lambda_for_ratio": (_i, [_p, _sz, ctypes.c_double, ctypes.c_double, _p, _p, _sz, _p]),
     "ssa_lambda_from_scale_factor": (_f, [_f, _i]),
     "ssa_status_string": (ctypes.c_char_p, [_i]),
     "ssa_abi_version": (_i, []),
@@ -200,8 +202,8 @@ def decode(q, k_cache, v_cache, seqlens, lam: float, split_tiles: int = 32, Bc: 
     nT = math.ceil(S_max / Bc)
     nS = math.ceil(nT / split_tiles)
     dev = q.device
-    need = decode_workspace_size(B, Hq, S_max, d, Bc, split_tiles)
     if workspace is None:
+        need = decode_workspace_size(B, Hq, S_max, d, Bc, split_tiles)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     res = {"workspace": workspace}
     res["out"] = out if out is not None else torch.empty_like(q)
@@ -364,3 +366,38 @@ def vertical_slash_mask(q, k, n_vertical: int, n_slash: int, last_q: int = 64, p
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check("ssa_vertical_slash_mask", st)
     return res
+
+
+def calibrate_workspace_size(n_margins: int, window: float = 0.01) -> int:
+    return int(lib().ssa_calibrate_workspace_size(int(n_margins), float(window)))
+
+
+def lambda_for_ratio(margins, target: float, window: float = 0.01, workspace=None, result=None,
+                     stream=None, sync: bool = True):
+    """Device threshold calibration (``ssa_lambda_for_ratio``) over a fp32
+    margin tensor (NaN = tile not visited). Returns (lambda, achieved ratio)
+    as Python floats after synchronising the stream, or, with ``sync=False``,
+    the device result tensor of 4 doubles (lambda, ratio, n, n below)."""
+    if not isinstance(margins, torch.Tensor) or margins.dtype != torch.float32 or not margins.is_cuda:
+        raise TypeError("margins must be a float32 device tensor")
+    if not margins.is_contiguous():
+        raise ValueError("margins must be contiguous")
+    n = margins.numel()
+    dev = margins.device
+    need = calibrate_workspace_size(n, window)
+    if need == 0:
+        raise ValueError("invalid calibration sizes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if result is None:
+        result = torch.empty(4, dtype=torch.float64, device=dev)
+    st = lib().ssa_lambda_for_ratio(
+        _ptr(margins), n, float(target), float(window), _ptr(result), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("ssa_lambda_for_ratio", st)
+    if not sync:
+        return result
+    r = result.cpu().tolist()
+    if math.isnan(r[0]):
+        raise RuntimeError("ssa_lambda_for_ratio: workspace bound exceeded")
+    return float(r[0]), float(r[1])

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libssa.so")
 
-SOURCES = ["ssa_api.cpp", "prefill.hip", "decode.hip", "mask.hip", "vslash.hip"]
+SOURCES = ["ssa_api.cpp", "prefill.hip", "decode.hip", "mask.hip", "vslash.hip", "calibrate.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -112,6 +112,22 @@ __device__ __forceinline__ void load_lds16_buf(__amdgpu_buffer_rsrc_t rsrc, uint
 // so that the compiler's own wait insertion knows the loads have landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until every global load (LDS-direct ones included) AND every LDS
+// access of this wave is done: vmcnt 0, lgkmcnt 0 (expcnt at its maximum).
+__device__ __forceinline__ void wait_vmem_lds() { __builtin_amdgcn_s_waitcnt(0x0070); }
+
+// Workgroup barrier for LDS hand-offs between waves. The release fence of
+// __syncthreads() is meant to wait for this wave's LDS writes, but where the
+// barrier heads a loop the compiler has been seen to drop that wait on the
+// back edge (an LDS write at the end of one iteration, the barrier at the
+// top of the next): the write could then land after another wave's read.
+// This barrier first waits for all of this wave's LDS operations (lgkmcnt 0)
+// with a wait the compiler keeps.
+__device__ __forceinline__ void sync_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __syncthreads();
+}
+
 // LDS transpose read (ds_read_b64_tr_b16): within each group of 16 lanes,
 // lane li receives element (li % 4) of the 8-byte chunks addressed by lanes
 // 4e + li / 4, for e = 0..3.

@@ -108,12 +108,24 @@ struct VsWorkspace {
   }
 };
 
+// Workspace of the device threshold calibration for n margins and a rank
+// window: byte offsets (256-byte aligned) of the state, the radix
+// histograms, the bucket minima and maxima (nb_max each) and the per-chunk
+// gap summaries.
+struct CalWorkspace {
+  long long nb_max;
+  size_t state, hist, bmin, bmax, sums, total;
+  CalWorkspace(long long n, double window);
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_block_mask(const MaskParams& p, hipStream_t stream);
 hipError_t launch_sparge_mask(const SpargeParams& p, hipStream_t stream);
 hipError_t launch_vertical_slash(const VsParams& p, hipStream_t stream);
+hipError_t launch_lambda_for_ratio(const float* margins, long long n, double target, double window,
+                                   double* result, void* workspace, hipStream_t stream);
 
 // Decode workspace layout: partial o [B, Hq, nS, d] fp32, then (m, l) [B, Hq, nS, 2] fp32.
 inline size_t decode_num_splits(int S_max, int Bc, int split_tiles) {

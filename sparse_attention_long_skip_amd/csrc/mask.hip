@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void pool_kernel(MaskArgs a) {
     part[0][rg][cc * 8 + e] = acc[e];
     if constexpr (SIM) part[SIM ? 1 : 0][rg][cc * 8 + e] = accn[e];
   }
-  __syncthreads();
+  sync_lds();
   const float n = (float)(r1 - r0);
   float un = 0.f;
   if (t < D) {
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void pool_kernel(MaskArgs a) {
     // self-similarity = squared norm of the mean unit row (threads >= D add 0)
     const float w = wave_sum(un * un);
     if ((t & (kWave - 1)) == 0) red[t / kWave] = w;
-    __syncthreads();
+    sync_lds();
     if (t == 0) {
       const float sim = red[0] + red[1] + red[2] + red[3];
       (is_k ? a.simk : a.simq)[hb * a.nB + blk] = sim;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void compress_k_kernel(MaskArgs a) {
     const int r = x / CPR, cc = x % CPR;
     store16(&rows[r][cc * 8], load16(src + (size_t)(r0 + r) * D + cc * 8));
   }
-  __syncthreads();
+  sync_lds();
   const int ch = t % D;
   for (int w = t / D; w < kWinPerBlock; w += 256 / D) {
     const int m = blk * kWinPerBlock + w;
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void select_kernel(MaskArgs a) {
 
   const size_t hb = (size_t)b * a.H + hh;
   for (int x = t; x < nq * D; x += NT) qv[x / D][x % D] = a.qbar[(hb * a.nB + qb0 + x / D) * D + x % D];
-  __syncthreads();
+  sync_lds();
 
   // Scores: each pooled key row is read once for all QPB query blocks. With
   // compressed keys a block's score is the best of its windows.
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(256) void select_kernel(MaskArgs a) {
     for (int q = 0; q < nq; ++q)
       for (int c = qb0 + q + 1 + t; c < a.nB; c += NT)
         a.block_scores[(hb * a.nB + qb0 + q) * a.nB + c] = -INFINITY;
-  __syncthreads();
+  sync_lds();
 
   // Selection: wave wv owns row qb0 + wv (QPB == 4 rows per workgroup, or
   // one row handled by wave 0). The top-k threshold is the topk-th largest

@@ -393,7 +393,10 @@ void prefill_kernel(PrefillArgs a) {
     const bool have_cur = tcur < n_list;
     const bool have_prev = jprev >= 0;
     if (!have_cur && !have_prev) return false;
-    wait_vmem();
+    // K(t) and the last kept V (LDS-direct loads) and the flags of tile t-1
+    // (LDS writes of the previous step, across the loop's back edge) must be
+    // complete before the barrier: one wait covers both counters.
+    wait_vmem_lds();
     __syncthreads();
     bool keep1 = false;     // some unit keeps tile jprev: exponentials, P.V, V load
     bool keep_mine = false;  // this wave's unit keeps it
@@ -566,7 +569,7 @@ void prefill_kernel(PrefillArgs a) {
   while (step(StepParity<0>{}) && step(StepParity<1>{})) {
   }
   // P.V of the last kept tile (of zeros if none was kept).
-  wait_vmem();
+  wait_vmem_lds();
   __syncthreads();
 #pragma unroll
   for (int c = 0; c < 4; ++c) pv_chunk(v_lds[VSINGLE ? 0 : vpar], c);

@@ -13,6 +13,7 @@ namespace {
 
 constexpr int kBc = 64;
 constexpr int kMaxMaskBlocks = 4096;
+constexpr size_t kMaxMargins = (size_t)1 << 40;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -399,6 +400,23 @@ int ssa_vertical_slash_mask(const void* q, const void* k, int B, int H, int L, i
   return hip_status(ssa::launch_vertical_slash(p, static_cast<hipStream_t>(stream)));
 }
 
+size_t ssa_calibrate_workspace_size(size_t n_margins, double window) {
+  if (n_margins > kMaxMargins || !(window >= 0.0 && window <= 0.5)) return 0;
+  return ssa::CalWorkspace((long long)n_margins, window).total;
+}
+
+int ssa_lambda_for_ratio(const float* margins, size_t n_margins, double target, double window,
+                         double* result, void* workspace, size_t workspace_bytes, void* stream) {
+  if ((n_margins > 0 && !margins) || !result) return SSA_ERR_INVALID_ARG;
+  if (n_margins > kMaxMargins) return SSA_ERR_INVALID_ARG;
+  if (!(target >= 0.0 && target <= 1.0) || !(window >= 0.0 && window <= 0.5)) return SSA_ERR_INVALID_ARG;
+  if (!aligned(margins, 4) || !aligned(result, 8)) return SSA_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 256)) return SSA_ERR_WORKSPACE;
+  if (workspace_bytes < ssa::CalWorkspace((long long)n_margins, window).total) return SSA_ERR_WORKSPACE;
+  return hip_status(ssa::launch_lambda_for_ratio(margins, (long long)n_margins, target, window, result,
+                                                 workspace, static_cast<hipStream_t>(stream)));
+}
+
 float ssa_lambda_from_scale_factor(float scale_factor, int L) {
   if (!(scale_factor > 0.f) || L <= 0) return NAN;
   const float lam = logf(scale_factor / (float)L);
@@ -416,6 +434,6 @@ const char* ssa_status_string(int status) {
   }
 }
 
-int ssa_abi_version(void) { return 100; }
+int ssa_abi_version(void) { return 101; }
 
 }  // extern "C"

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void vs_pass(VsArgs a) {
     float dsum[2] = {0.f, 0.f};  // diagonals e = t and e = t + 256
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      __syncthreads();  // the previous half has been read
+      sync_lds();  // the previous half has been read
       const int i = rb * 32 + col;
       const int p = a.L - a.R + i;
 #pragma unroll
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void vs_pass(VsArgs a) {
           A_lds[col][jl] = ok ? fast_exp2(acc[gi][rb][r] * a.c_log2 - mrow[rb]) * invl[rb] : 0.f;
         }
       }
-      __syncthreads();
+      sync_lds();
       const int r_lo = rb * 32, r_hi = min(a.R, rb * 32 + 32);  // rows of this half
       if (j0 + t < a.L)
         for (int r = r_lo; r < r_hi; ++r) csum += A_lds[r - r_lo][t];
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void vs_pass(VsArgs a) {
         red[wv][rb * 32 + col][1] = l;
       }
     }
-    __syncthreads();
+    sync_lds();
     if (t < 64) {
       float mx = -INFINITY;
       for (int w = 0; w < 4; ++w) mx = fmaxf(mx, red[w][t][0]);
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(1024) void vs_rowstats(VsArgs a) {
   }
   red[sl][i][0] = mx;
   red[sl][i][1] = l;
-  __syncthreads();
+  sync_lds();
   if (sl != 0 || i >= a.R) return;
   float m = -INFINITY;
   for (int k = 0; k < NSL; ++k) m = fmaxf(m, red[k][i][0]);
@@ -285,9 +285,9 @@ __device__ int block_exclusive_scan(int x, int* scratch) {
     const int y = __shfl_up(inc, o, kWave);
     if (lane >= o) inc += y;
   }
-  __syncthreads();
+  sync_lds();
   if (lane == 63) scratch[w] = inc;
-  __syncthreads();
+  sync_lds();
   int before = 0;
   for (int i = 0; i < w; ++i) before += scratch[i];
   return before + inc - x;
@@ -304,9 +304,9 @@ __device__ uint64_t block_exclusive_scan64(uint64_t x, uint64_t* scratch, uint64
     const uint32_t hi = __shfl_up((uint32_t)(inc >> 32), o, kWave);
     if (lane >= o) inc += ((uint64_t)hi << 32) | lo;
   }
-  __syncthreads();
+  sync_lds();
   if (lane == 63) scratch[w] = inc;
-  __syncthreads();
+  sync_lds();
   uint64_t before = 0, all = 0;
 #pragma unroll
   for (int i = 0; i < SEL_T / 64; ++i) {
@@ -356,7 +356,7 @@ __global__ __launch_bounds__(SEL_T) void vs_select(VsArgs a) {
   if (by_rank) {
     for (int shift = 24; shift >= 0; shift -= 8) {
       for (int e = t; e < NCOPY * HS; e += SEL_T) hist[e] = 0;
-      __syncthreads();
+      sync_lds();
       int* mine = hist + (t & (NCOPY - 1)) * HS;
       if (in_reg) {
 #pragma unroll
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(SEL_T) void vs_select(VsArgs a) {
           }
         }
       }
-      __syncthreads();
+      sync_lds();
       // thread t looks at digit 255 - t: suffix count S = excl + own
       int own = 0;
       if (t < 256)
@@ -389,11 +389,11 @@ __global__ __launch_bounds__(SEL_T) void vs_select(VsArgs a) {
         pick[0] = 255 - t;
         pick[1] = need - excl;
       }
-      __syncthreads();
+      sync_lds();
       thr |= (uint32_t)pick[0] << shift;
       mask |= 255u << shift;
       need = pick[1];
-      __syncthreads();  // pick is rewritten next pass
+      sync_lds();  // pick is rewritten next pass
     }
   }
   const int need_eq = by_rank ? need : 0;

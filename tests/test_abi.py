@@ -36,7 +36,7 @@ def test_status_strings_and_helpers(lib):
     import sparse_attention_long_skip_amd as ssa
     for st in (0, -1, -2, -3, -4):
         assert ssa.status_string(st).startswith("SSA")
-    assert ssa.abi_version() == 100
+    assert ssa.abi_version() == 101
     lam = ssa.lambda_from_scale_factor(1000.0, 131072)
     assert abs(lam - math.log(1000.0 / 131072)) < 1e-5
     assert ssa.lambda_from_scale_factor(1e9, 10) == 0.0
