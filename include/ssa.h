@@ -46,6 +46,7 @@ extern "C" {
 #define SSA_ERR_UNSUPPORTED (-2) /* valid but not built: head dim, tile sizes, group size */
 #define SSA_ERR_WORKSPACE (-3)   /* workspace null or smaller than the *_workspace_size value */
 #define SSA_ERR_HIP (-4)         /* the HIP runtime reported an error at launch */
+#define SSA_ERR_SCRATCH (-5)     /* needs more than the static scratch of ssa_decode_noalloc */
 
 /* Values written into the optional per-tile decision arrays. */
 #define SSA_TILE_KEPT 1
@@ -148,6 +149,32 @@ int ssa_decode(const void* q, const void* k_cache, const void* v_cache, const in
                float* tile_margin, int B, int Hq, int Hkv, int S_max, int d, int Bc,
                int split_tiles, float lambda, void* workspace, size_t workspace_bytes,
                void* stream);
+
+/* Size of the static device scratch behind ssa_decode_noalloc (16 MiB). */
+#define SSA_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * ssa_decode_noalloc -- ssa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. Same arguments, results and errors as ssa_decode,
+ * without the workspace: the split partials live in a static device array
+ * of SSA_DECODE_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends (its address is looked up once per device, on
+ * that device's first call). Nothing is allocated or freed, by the library
+ * or by any routine it calls.
+ *  - Calls whose ssa_decode_workspace_size(...) exceeds
+ *    SSA_DECODE_SCRATCH_BYTES return SSA_ERR_SCRATCH and enqueue nothing
+ *    (for example B = 32, Hq = 32, S_max = 32768, d = 128, split_tiles = 24
+ *    needs 11.7 MB and fits).
+ *  - All calls on one GPU share that GPU's scratch: calls that overlap on a
+ *    GPU (different streams, or host threads without ordering) race. Calls
+ *    ordered on one stream are safe. No scratch content needs to start at
+ *    zero: every partial the combine reads is written by the same call.
+ */
+int ssa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
+                       void* out, float* lse, int32_t* skip_counts, uint8_t* tile_state,
+                       float* tile_margin, int B, int Hq, int Hkv, int S_max, int d, int Bc,
+                       int split_tiles, float lambda, void* stream);
 
 /*
  * ssa_block_mask_max_blocks -- length of the kept-block list per query block

@@ -23,6 +23,8 @@ SSA_ERR_INVALID_ARG = -1
 SSA_ERR_UNSUPPORTED = -2
 SSA_ERR_WORKSPACE = -3
 SSA_ERR_HIP = -4
+SSA_ERR_SCRATCH = -5
+DECODE_SCRATCH_BYTES = 16 << 20
 TILE_KEPT = 1
 TILE_SKIPPED = 2
 
@@ -38,6 +40,7 @@ _SIGNATURES = {
     "ssa_prefill_nm": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _i, _i, _p]),
     "ssa_decode_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "ssa_decode": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _sz, _p]),
+    "ssa_decode_noalloc": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p]),
     "ssa_block_mask_max_blocks": (_i, [_i, _i, _i, _i, _i]),
     "ssa_block_mask_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
     "ssa_block_mask": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i, _p, _p, _sz, _p]),
@@ -188,11 +191,13 @@ def decode_workspace_size(B, Hq, S_max, d, Bc=64, split_tiles=32) -> int:
 
 def decode(q, k_cache, v_cache, seqlens, lam: float, split_tiles: int = 32, Bc: int = 64,
            workspace=None, lse: bool = True, stats: bool = False, margins: bool = False,
-           out=None, stream=None, lse_out=None, skip_counts=None, counts: bool = False) -> dict:
+           out=None, stream=None, lse_out=None, skip_counts=None, counts: bool = False,
+           noalloc: bool = False) -> dict:
     """Skip-Softmax split-K decode (``ssa_decode``). q [B,Hq,d]; caches
     [B,Hkv,S_max,d] bf16; seqlens [B] int32 (device). ``stats`` asks for
     skip_counts and tile_state, ``counts`` for skip_counts alone; ``lse_out``
-    and ``skip_counts`` may be caller-provided tensors."""
+    and ``skip_counts`` may be caller-provided tensors. ``noalloc`` calls
+    ``ssa_decode_noalloc`` (the library's static scratch, no workspace)."""
     _need(q, "q", torch.bfloat16, 3)
     _need(k_cache, "k_cache", torch.bfloat16, 4)
     _need(v_cache, "v_cache", torch.bfloat16, 4)
@@ -202,7 +207,10 @@ def decode(q, k_cache, v_cache, seqlens, lam: float, split_tiles: int = 32, Bc: 
     nT = math.ceil(S_max / Bc)
     nS = math.ceil(nT / split_tiles)
     dev = q.device
-    if workspace is None:
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace")
+    elif workspace is None:
         need = decode_workspace_size(B, Hq, S_max, d, Bc, split_tiles)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     res = {"workspace": workspace}
@@ -223,6 +231,13 @@ def decode(q, k_cache, v_cache, seqlens, lam: float, split_tiles: int = 32, Bc: 
     res["tile_state"] = torch.zeros((B, Hkv, nT), dtype=torch.uint8, device=dev) if stats else None
     res["tile_margin"] = (torch.full((B, Hkv, nT), float("nan"), dtype=torch.float32, device=dev)
                           if margins else None)
+    if noalloc:
+        st = lib().ssa_decode_noalloc(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(res["out"]), _ptr(res["lse"]),
+            _ptr(res["skip_counts"]), _ptr(res["tile_state"]), _ptr(res["tile_margin"]),
+            B, Hq, Hkv, S_max, d, Bc, split_tiles, float(lam), _stream(stream))
+        _check("ssa_decode_noalloc", st)
+        return res
     st = lib().ssa_decode(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(res["out"]), _ptr(res["lse"]),
         _ptr(res["skip_counts"]), _ptr(res["tile_state"]), _ptr(res["tile_margin"]),

@@ -15,6 +15,8 @@
 // P.V runs on the vector units: V rows are read with coalesced 16-byte loads
 // (each row is 16 lanes x 16 B at d = 128) and the probabilities come from a
 // small per-wave LDS table.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -322,6 +324,36 @@ hipError_t launch_g(const DecodeArgs& a, int G, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Scratch of the allocation-free decode entry point: the split partials
+// live in this file-scope device array instead of a caller workspace. Every
+// GPU the library runs on holds its own copy for the life of the process;
+// all such calls on one GPU share it (calls that overlap on a GPU race).
+__device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_addr[dev] == nullptr) {
+    // The array's name is a host-side stand-in; its device address on the
+    // current device comes from the runtime, once per device.
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_addr[dev] = addr;
+  }
+  *ptr = scratch_addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   DecodeArgs a;

@@ -9,6 +9,8 @@
 
 #include "launch.h"
 
+static_assert(ssa::kDecodeScratchBytes == SSA_DECODE_SCRATCH_BYTES, "scratch size");
+
 namespace {
 
 constexpr int kBc = 64;
@@ -264,6 +266,42 @@ int ssa_decode(const void* q, const void* k_cache, const void* v_cache, const in
   return hip_status(ssa::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 
+int ssa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
+                       void* out, float* lse, int32_t* skip_counts, uint8_t* tile_state,
+                       float* tile_margin, int B, int Hq, int Hkv, int S_max, int d, int Bc,
+                       int split_tiles, float lambda, void* stream) {
+  // Validate as ssa_decode, with a stand-in workspace that passes its checks;
+  // then the size against the static scratch.
+  const size_t need_ok = (size_t)1 << 62;
+  int st = check_decode(q, k_cache, v_cache, seqlens, out, B, Hq, Hkv, S_max, d, Bc, split_tiles, lambda,
+                        reinterpret_cast<void*>(uintptr_t(256)), need_ok);
+  if (st != SSA_OK) return st;
+  if (ssa::decode_workspace_bytes(B, Hq, S_max, d, Bc, split_tiles) > SSA_DECODE_SCRATCH_BYTES)
+    return SSA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (ssa::decode_scratch(&ws) != hipSuccess) return SSA_ERR_HIP;
+  ssa::DecodeParams p;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.seqlens = seqlens;
+  p.out = out;
+  p.lse = lse;
+  p.skip_counts = skip_counts;
+  p.tile_state = tile_state;
+  p.tile_margin = tile_margin;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.S_max = S_max;
+  p.d = d;
+  p.Bc = Bc;
+  p.split_tiles = split_tiles;
+  p.lambda = lambda;
+  p.workspace = ws;
+  return hip_status(ssa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
 int ssa_block_mask_max_blocks(int L, int pool, int topk, int sink_blocks, int window_tokens) {
   return mask_max_blocks(L, pool, topk, sink_blocks, window_tokens);
 }
@@ -430,6 +468,9 @@ const char* ssa_status_string(int status) {
     case SSA_ERR_UNSUPPORTED: return "SSA_ERR_UNSUPPORTED: configuration not built";
     case SSA_ERR_WORKSPACE: return "SSA_ERR_WORKSPACE: workspace missing or too small";
     case SSA_ERR_HIP: return "SSA_ERR_HIP: HIP launch error";
+    case SSA_ERR_SCRATCH:
+      return "SSA_ERR_SCRATCH: the call needs more than the library's static scratch "
+             "(SSA_DECODE_SCRATCH_BYTES); use the entry point that takes a workspace";
     default: return "SSA: unknown status";
   }
 }

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings_and_helpers(lib):
     import sparse_attention_long_skip_amd as ssa
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert ssa.status_string(st).startswith("SSA")
     assert ssa.abi_version() == 101
     lam = ssa.lambda_from_scale_factor(1000.0, 131072)
@@ -93,6 +93,32 @@ def test_decode_validation(lib):
     assert _decode(lib, d=80) == -2
     assert _decode(lib, ws=None) == -3
     assert _decode(lib, wsb=16) == -3
+
+
+def _decode_noalloc(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, sl=FAKE, out=FAKE, B=2, Hq=8, Hkv=2, S=1024, d=128, Bc=64,
+             T=4, lam=-1.0)
+    a.update(kw)
+    return lib.ssa_decode_noalloc(a["q"], a["kc"], a["vc"], a["sl"], a["out"], None, None, None, None,
+                                  a["B"], a["Hq"], a["Hkv"], a["S"], a["d"], a["Bc"], a["T"],
+                                  ctypes.c_float(a["lam"]), None)
+
+
+def test_decode_noalloc_validation(lib):
+    import sparse_attention_long_skip_amd as ssa
+    # the decode checks apply unchanged
+    assert _decode_noalloc(lib, sl=None) == -1
+    assert _decode_noalloc(lib, T=0) == -1
+    assert _decode_noalloc(lib, lam=1.0) == -1
+    assert _decode_noalloc(lib, Hq=12, Hkv=4) == -2
+    # partials beyond the static scratch are refused before any HIP call:
+    # B=16, Hq=32, S_max=8192, split 2 tiles -> 64 splits of 130 floats = 17.0 MB
+    need = ssa.decode_workspace_size(16, 32, 8192, 128, 64, 2)
+    assert need > ssa.DECODE_SCRATCH_BYTES
+    assert _decode_noalloc(lib, B=16, Hq=32, Hkv=8, S=8192, T=2) == ssa.SSA_ERR_SCRATCH
+    assert ssa.status_string(ssa.SSA_ERR_SCRATCH).startswith("SSA_ERR_SCRATCH")
+    # the 32-sequence decode workload fits
+    assert ssa.decode_workspace_size(32, 32, 32768, 128, 64, 24) <= ssa.DECODE_SCRATCH_BYTES
 
 
 def _mask(lib, **kw):
