@@ -551,7 +551,10 @@ def extra_nm(args, torch, np, ssa, synth):
 
 def extra_warp_units(args, torch, np, ssa, synth):
     """Br = 32 decision units (the per-warp variant) on the 16K GQA shape,
-    lambda calibrated to ~50% of the 32-row units' tiles skipped."""
+    lambda calibrated to ~50% of the 32-row units' tiles skipped. Four units
+    share a 128-row workgroup: every wave computes the scores of the tiles
+    the workgroup visits, and the exponentials and P.V of the tiles its own
+    unit keeps."""
     from sparse_attention_long_skip_amd.calibrate import calibrate_prefill
     c = synth.CONFIGS[1]
     x = synth.prefill_inputs(1, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"], frac=c["frac"])
@@ -559,22 +562,12 @@ def extra_warp_units(args, torch, np, ssa, synth):
     del x
     kw = dict(Br=32, Bc=c["Bc"], causal=True)
     lam, _ = calibrate_prefill(q, k, v, 0.5, **kw)
-    st = ssa.prefill(q, k, v, lam, stats=True, **kw)
-    torch.cuda.synchronize()
-    s = st["tile_state"].cpu().numpy()  # [B, Hq, L / 32, nK]
-    vis, kept = int((s != 0).sum()), int((s == 1).sum())
-    # four 32-row units share a 128-row workgroup: every wave computes the
-    # scores of the tiles the workgroup visits and the P.V of the tiles any
-    # of its units keeps
-    g = s.reshape(s.shape[0], s.shape[1], -1, 4, s.shape[-1])
-    wg_vis = int((g != 0).any(axis=3).sum())
-    wg_kept = int((g == 1).any(axis=3).sum())
-    out = torch.empty_like(q)
-    ms, ev = time_launches(lambda: ssa.prefill(q, k, v, lam, out=out, **kw), 10, 3, torch)
-    ex = 2.0 * 32 * 64 * c["d"] * 4 * (wg_vis + wg_kept)
+    vis, kept, ms, ev = time_prefill_legs(q, k, v, lam, kw, 10, 3, torch, ssa)
+    wg_vis = visited_tiles_count(c["B"], c["Hq"], c["L"], 128, c["Bc"], True)
+    ex = 2.0 * 32 * 64 * c["d"] * (4 * wg_vis + kept)
     return {"workload": "Br=32 decision units (per-warp skip), 16K GQA shape, lambda calibrated to ~50% unit skip",
             "lambda": round(lam, 5), "ms": round(ms, 4), "skip_pct": round(100.0 * (vis - kept) / vis, 3),
-            "pv_tiles_run_vs_kept": round(4 * wg_kept / max(kept, 1), 3),
+            "unit_tiles_visited": vis, "unit_tiles_kept": kept, "workgroup_tiles_visited": wg_vis,
             "dense_equiv_tflops": round(dense_flops(c) / ms / 1e9, 1),
             "mfma_frac_executed": round(ex / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 

@@ -81,8 +81,14 @@ extern "C" {
  *  block_idx [B, Hq, nQ, max_blocks] int32, nullable: for query tile i the
  *           first block_cnt[b,h,i] entries are the key tiles to visit, in
  *           visit order (ascending expected). Entries < 0, >= nK or above the
- *           causal limit are ignored. block_cnt [B, Hq, nQ] int32 is required
- *           with block_idx; counts are clamped to [0, max_blocks].
+ *           causal limit are ignored. Entries should be unique: a repeated
+ *           entry is visited again, so its keys count twice in the softmax
+ *           (the mask builders of this library never repeat one).
+ *           block_cnt [B, Hq, nQ] int32 is required with block_idx; counts
+ *           are clamped to [0, max_blocks]. With Br = 64 two query tiles
+ *           share a workgroup: when both lists are ascending they are merged
+ *           (a tile on both is loaded once), otherwise visited one after the
+ *           other; either way each tile keeps its own list order.
  *
  * Returns SSA_OK or a negative status.
  */

@@ -41,7 +41,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kScanThreads = 1024;
-constexpr int kChunk = 64;  // buckets per thread in the gap scan
+constexpr int kChunk = 16;  // buckets per thread in the gap scan
 
 struct CalState {
   unsigned long long n_valid, n_neginf, n_posinf, n_below;
@@ -366,10 +366,18 @@ __global__ __launch_bounds__(kScanThreads) void cal_gap_final(CalState* st, cons
   s.first_min = s.last_max = s.best_a = s.best_b = 0.f;
   for (long long c = t * per; c < (t + 1) * per && c < nchunk; ++c) gap_merge(s, sum[c]);
   part[t] = s;
-  sync_lds();
+  // ordered tree merge: part[t] absorbs part[t + h] (the merge is
+  // associative and keeps the first of equal gaps)
+  for (int h = 1; h < kScanThreads; h <<= 1) {
+    sync_lds();
+    if ((t & (2 * h - 1)) == 0) {
+      GapSummary a = part[t];
+      gap_merge(a, part[t + h]);
+      part[t] = a;
+    }
+  }
   if (t == 0) {
-    GapSummary a = part[0];
-    for (int i = 1; i < kScanThreads; ++i) gap_merge(a, part[i]);
+    const GapSummary a = part[0];
     const double lam = 0.5 * ((double)a.best_a + (double)a.best_b);
     st->lambda = lam < 0.0 ? lam : 0.0;
     st->done = 1;

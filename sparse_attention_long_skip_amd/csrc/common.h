@@ -25,6 +25,14 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16x16x32 bf16 matrix-core product, fp32 accumulate. Operand layout (lane
+// l, group q = l / 16): A supplies row (l % 16) and reduction indices
+// 8q..8q+7; B supplies column (l % 16) and the same reduction indices; the
+// accumulator holds column (l % 16) and rows 4q + i for element i.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 __device__ __forceinline__ u32x4 as_u32x4(bf16x8 x) { return __builtin_bit_cast(u32x4, x); }
 

@@ -8,13 +8,15 @@
 // log-sum-exp identity.
 //
 // Design: one wave per (sequence, KV head, split), so the vote and the
-// softmax never need a workgroup barrier. Scores use 32x32x16 bf16 MFMA
+// softmax never need a workgroup barrier. Scores use 16x16x32 bf16 MFMA
 // (S^T = K Q^T, K rows read straight from HBM as the A operand, the G query
 // rows as B-operand columns). The K tile for step j+1 is prefetched into
-// registers while step j runs; the V tile is issued only after the vote.
+// registers while step j runs; the V tile is issued only after the vote,
+// and its P.V waits until the scores and vote of the next tile are done.
 // P.V runs on the vector units: V rows are read with coalesced 16-byte loads
 // (each row is 16 lanes x 16 B at d = 128) and the probabilities come from a
-// small per-wave LDS table.
+// small per-wave LDS table. Splits are dispatched split-major (every first
+// split, then every second one, ...), so the short last splits run last.
 #include <mutex>
 
 #include "common.h"
@@ -50,20 +52,24 @@ struct DecodeArgs {
 template <int D, int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((D == 128 ? G <= 4 : G <= 8) ? 2 : 1)))
 void decode_split_kernel(DecodeArgs a) {
-  constexpr int NKK = D / 16;
+  constexpr int NDS = D / 32;    // 32-wide reduction steps of the 16x16x32 products
   constexpr int CPR = D / 8;     // 16-byte chunks per V row
   constexpr int RG = 64 / CPR;   // row groups across the wave
   constexpr int KPG = BC / RG;   // keys per row group and tile
 
-  __shared__ __attribute__((aligned(16))) float p_lds[G][BC];
-  __shared__ float alpha_lds[G];
+  // P and the rescale factor of a kept tile, double-buffered: the next kept
+  // tile's are written while the pending tile's P.V still reads them.
+  __shared__ __attribute__((aligned(16))) float p_lds[2][G][BC];
+  __shared__ float alpha_lds[2][G];
 
   const int lane = threadIdx.x;
-  const int h = lane >> 5;
-  const int r32 = lane & 31;
-  const int sp = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  const int c16 = lane & 15;  // score column = query row g
+  const int q4 = lane >> 4;   // lane group: keys 4 q4 .. 4 q4 + 3 of each 16-key block
+  // Split-major order: all first splits are dispatched before any second
+  // split, so the short last splits of the sequences come at the end.
+  const int kvh = blockIdx.x;
+  const int b = blockIdx.y;
+  const int sp = blockIdx.z;
 
   const int n = min(max(a.seqlens[b], 0), a.S_max);
   const int ntiles = (n + BC - 1) / BC;
@@ -80,25 +86,28 @@ void decode_split_kernel(DecodeArgs a) {
   const uint16_t* vp = a.vc + ((size_t)b * a.Hkv + kvh) * a.S_max * D;
   const int hq0 = kvh * G;
 
-  // Query rows as B-operand columns (columns >= G are zero).
-  bf16x8 qf[NKK];
+  // S^T = K Q^T with 16x16x32 products: K rows (16 keys per block) are the
+  // A operand, the G query rows the B-operand columns (columns >= G zero).
+  // A lane then holds 4 consecutive keys of each 16-key block for one query
+  // row, and each K load covers 16 rows x 64 contiguous bytes.
+  bf16x8 qf[NDS];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
+  for (int ds = 0; ds < NDS; ++ds) {
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (r32 < G) x = load16(a.q + ((size_t)b * a.Hq + hq0 + r32) * D + kk * 16 + h * 8);
-    qf[kk] = as_bf16x8(x);
+    if (c16 < G) x = load16(a.q + ((size_t)b * a.Hq + hq0 + c16) * D + ds * 32 + q4 * 8);
+    qf[ds] = as_bf16x8(x);
   }
 
-  u32x4 kreg[2][NKK];
+  u32x4 kreg[4][NDS];
   auto load_k = [&](int j) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = j * BC + kb * 32 + r32;
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key = j * BC + kb * 16 + c16;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
+      for (int ds = 0; ds < NDS; ++ds) {
         u32x4 x = {0u, 0u, 0u, 0u};
-        if (key < n) x = load16(kp + (size_t)key * D + kk * 16 + h * 8);
-        kreg[kb][kk] = x;
+        if (key < n) x = load16(kp + (size_t)key * D + ds * 32 + q4 * 8);
+        kreg[kb][ds] = x;
       }
     }
   };
@@ -114,34 +123,66 @@ void decode_split_kernel(DecodeArgs a) {
   float l_acc = 0.f;
   int skipped = 0;
 
+  // The V rows of a kept tile are loaded right after its vote, and its P.V
+  // runs one step later, after the scores and the vote of the next tile:
+  // the V load has the next tile's matrix work to land behind.
+  u32x4 vreg[KPG];
+  bool pend = false;  // a kept tile awaits its P.V (V in vreg, P and alpha in LDS buffer pb)
+  int pb = 0;
+  auto pv_pending = [&]() __attribute__((always_inline)) {
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float al = alpha_lds[pb][g];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[g][e] *= al;
+    }
+#pragma unroll
+    for (int m4 = 0; m4 < KPG; m4 += 4) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const f32x4 pg = *reinterpret_cast<const f32x4*>(&p_lds[pb][g][rg * KPG + m4]);
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          const u32x4 vv = vreg[m4 + mm];
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            o[g][2 * e2] = fmaf(pg[mm], bf16_lo(vv[e2]), o[g][2 * e2]);
+            o[g][2 * e2 + 1] = fmaf(pg[mm], bf16_hi(vv[e2]), o[g][2 * e2 + 1]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  };
+
   load_k(j0);
   for (int j = j0; j < j1; ++j) {
-    f32x16 s[2];
+    f32x4 s[4];  // keys kb * 16 + 4 q4 + i of query row c16
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) s[kb] = mfma32(as_bf16x8(kreg[kb][kk]), qf[kk], s[kb]);
+      for (int ds = 0; ds < NDS; ++ds) s[kb] = mfma16(as_bf16x8(kreg[kb][ds]), qf[ds], s[kb]);
     }
     if (j + 1 < j1) load_k(j + 1);
     const int kbase = j * BC;
     if (kbase + BC > n) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kbase + kb * 32 + (e >> 2) * 8 + h * 4 + (e & 3);
-          if (key >= n) s[kb][e] = -INFINITY;
-        }
+        for (int e = 0; e < 4; ++e)
+          if (kbase + kb * 16 + q4 * 4 + e >= n) s[kb][e] = -INFINITY;
     }
     float mloc = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mloc = fmaxf(mloc, s[kb][e]);
-    mloc = fmaxf(mloc, swap_halves(mloc));
+      for (int e = 0; e < 4; ++e) mloc = fmaxf(mloc, s[kb][e]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
     float gap;
-    if (r32 >= G || mloc == -INFINITY) gap = -INFINITY;
+    if (c16 >= G || mloc == -INFINITY) gap = -INFINITY;
     else if (m_prev == -INFINITY) gap = INFINITY;
     else gap = mloc - m_prev;
     const float gw = wave_max(gap);
@@ -156,8 +197,30 @@ void decode_split_kernel(DecodeArgs a) {
       m_prev = fmaxf(m_prev, mloc);
       continue;
     }
-    // V rows of this lane's group: keys kbase + rg*KPG + m, d chunk cc.
-    u32x4 vreg[KPG];
+    // Exponentials of this tile into the other P buffer (the scores are then
+    // dead), the P.V of the pending tile, then this tile's V rows -- keys
+    // kbase + rg*KPG + m, d chunk cc -- into the registers it freed.
+    const int nb = pb ^ (pend ? 1 : 0);
+    const float m_new = fmaxf(m_prev, mloc);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2((m_prev - m_use) * a.c_log2);
+    const float mc = m_use * a.c_log2;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      f32x4 pv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pv[e] = fast_exp2(fmaf(s[kb][e], a.c_log2, -mc));
+        psum += pv[e];
+      }
+      if (c16 < G) *reinterpret_cast<f32x4*>(&p_lds[nb][c16][kb * 16 + q4 * 4]) = pv;
+    }
+    l_acc = l_acc * alpha + psum;
+    m_prev = m_new;
+    if (lane < G) alpha_lds[nb][lane] = alpha;
+    if (pend) pv_pending();
+    pb = nb;
 #pragma unroll
     for (int m = 0; m < KPG; ++m) {
       const int key = kbase + rg * KPG + m;
@@ -165,52 +228,9 @@ void decode_split_kernel(DecodeArgs a) {
       if (key < n) x = load16(vp + (size_t)key * D + cc * 8);
       vreg[m] = x;
     }
-    const float m_new = fmaxf(m_prev, mloc);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2((m_prev - m_use) * a.c_log2);
-    const float mc = m_use * a.c_log2;
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 pv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pv[e] = fast_exp2(fmaf(s[kb][q4 * 4 + e], a.c_log2, -mc));
-          psum += pv[e];
-        }
-        if (r32 < G)
-          *reinterpret_cast<f32x4*>(&p_lds[r32][kb * 32 + q4 * 8 + h * 4]) = pv;
-      }
-    l_acc = l_acc * alpha + psum;
-    m_prev = m_new;
-    if (lane < G) alpha_lds[lane] = alpha;
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float al = alpha_lds[g];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[g][e] *= al;
-    }
-#pragma unroll
-    for (int m4 = 0; m4 < KPG; m4 += 4) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const f32x4 pg = *reinterpret_cast<const f32x4*>(&p_lds[g][rg * KPG + m4]);
-#pragma unroll
-        for (int mm = 0; mm < 4; ++mm) {
-          const u32x4 vv = vreg[m4 + mm];
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            o[g][2 * e2] = fmaf(pg[mm], bf16_lo(vv[e2]), o[g][2 * e2]);
-            o[g][2 * e2 + 1] = fmaf(pg[mm], bf16_hi(vv[e2]), o[g][2 * e2 + 1]);
-          }
-        }
-      }
-    }
-    __syncthreads();
+    pend = true;
   }
+  if (pend) pv_pending();
 
   // Reduce o over the row groups (lanes with equal chunk index).
 #pragma unroll
@@ -219,7 +239,8 @@ void decode_split_kernel(DecodeArgs a) {
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[g][e] += __shfl_xor(o[g][e], off, kWave);
-  const float l_tot = l_acc + swap_halves(l_acc);
+  float l_tot = l_acc + __shfl_xor(l_acc, 16, kWave);
+  l_tot += __shfl_xor(l_tot, 32, kWave);
   const size_t base = ((size_t)b * a.Hq + hq0) * a.nS + sp;
   if (rg == 0) {
 #pragma unroll
@@ -231,19 +252,21 @@ void decode_split_kernel(DecodeArgs a) {
       *reinterpret_cast<f32x4*>(dst + 4) = x1;
     }
   }
-  if (r32 < G && h == 0) {
-    float* ml = a.ws_ml + (base + (size_t)r32 * a.nS) * 2;
+  if (lane < G) {
+    float* ml = a.ws_ml + (base + (size_t)lane * a.nS) * 2;
     ml[0] = m_prev;
     ml[1] = l_tot;
   }
   if (a.skip_counts && lane == 0) a.skip_counts[unit_s] = skipped;
 }
 
-// One workgroup per (query head, sequence): merge the split partials. The
-// partials are read 16 splits at a time with every load issued before the
-// first use (a loop that waited on each load in turn was latency-bound).
+// One workgroup per (query head, sequence) merges the split partials in one
+// pass: thread t (< D) keeps the log-sum-exp of the splits seen so far and
+// the output element t weighted against it, rescaling both when a split
+// raises the maximum; the partials are read 16 splits per batch of loads
+// (every load issued before the first use).
 template <int D>
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   constexpr int U = 16;
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
@@ -252,62 +275,51 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
   const int ntiles = (n + BC - 1) / BC;
   const int nsp = (ntiles + a.T - 1) / a.T;
   const size_t base = ((size_t)b * a.Hq + hq) * a.nS;
-  // lse = log sum_s exp(lse_s), lse_s = m_s / sqrt(d) + ln l_s over the
-  // splits with l_s > 0 (running max and rescaled sum, one split at a time).
-  float top = -INFINITY, tot = 0.f;
+  // lse_s = m_s / sqrt(d) + ln l_s over the splits with l_s > 0;
+  // top = max lse_s, tot = sum exp(lse_s - top),
+  // acc = sum exp(m_s / sqrt(d) - top) o_s[t].
+  float top = -INFINITY, tot = 0.f, acc = 0.f;
   for (int s0 = 0; s0 < nsp; s0 += U) {
-    float mm[U], ll[U];
+    float mm[U], ll[U], oo[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool ok = s0 + u < nsp;
       mm[u] = ok ? a.ws_ml[(base + s0 + u) * 2] : 0.f;
       ll[u] = ok ? a.ws_ml[(base + s0 + u) * 2 + 1] : 0.f;
+      oo[u] = ok ? a.ws_o[(base + s0 + u) * D + t] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (ll[u] > 0.f) {
-        const float x = mm[u] * a.inv_sqrt_d + __logf(ll[u]);
+        const float ms = mm[u] * a.inv_sqrt_d;
+        const float x = ms + __logf(ll[u]);
         if (x > top) {
-          tot = tot * __expf(top - x) + 1.f;
+          const float sc = __expf(top - x);
+          tot = tot * sc + 1.f;
+          acc = acc * sc + __expf(ms - x) * oo[u];
           top = x;
         } else {
           tot += __expf(x - top);
+          acc += __expf(ms - top) * oo[u];
         }
       }
     }
   }
   const float lse = (tot > 0.f) ? top + __logf(tot) : -INFINITY;
-  if (t < D) {
-    float acc = 0.f;
-    if (tot > 0.f) {
-      for (int s0 = 0; s0 < nsp; s0 += U) {
-        float mm[U], ll[U], oo[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const bool ok = s0 + u < nsp;
-          mm[u] = ok ? a.ws_ml[(base + s0 + u) * 2] : 0.f;
-          ll[u] = ok ? a.ws_ml[(base + s0 + u) * 2 + 1] : 0.f;
-          oo[u] = ok ? a.ws_o[(base + s0 + u) * D + t] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (ll[u] > 0.f) acc += __expf(mm[u] * a.inv_sqrt_d - lse) * oo[u];
-      }
-    }
-    const __bf16 r = (__bf16)acc;
-    a.out[((size_t)b * a.Hq + hq) * D + t] = __builtin_bit_cast(uint16_t, r);
-  }
+  const float r = tot > 0.f ? acc / tot : 0.f;
+  const __bf16 rb = (__bf16)r;
+  a.out[((size_t)b * a.Hq + hq) * D + t] = __builtin_bit_cast(uint16_t, rb);
   if (a.lse && t == 0) a.lse[(size_t)b * a.Hq + hq] = lse;
 }
 
 template <int D, int G>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
-  dim3 g1(a.nS, a.Hkv, a.B);
+  dim3 g1(a.Hkv, a.B, a.nS);
   hipLaunchKernelGGL((decode_split_kernel<D, G>), g1, dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(a.Hq, a.B);
-  hipLaunchKernelGGL((decode_combine_kernel<D>), g2, dim3(128), 0, stream, a);
+  hipLaunchKernelGGL((decode_combine_kernel<D>), g2, dim3(D), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(BR * 2) __attribute__((amdgpu_waves_per_eu(D == 64 
 void prefill_kernel(PrefillArgs a) {
   constexpr int NW = BR / 32;
   constexpr int NU = NW / UW;  // decision units per workgroup
-  static_assert(NU * UW == NW && (!SPARSE || NU == 1), "unit layout");
+  static_assert(NU * UW == NW && (!SPARSE || NU <= 2), "unit layout");
   constexpr int NT = NW * kWave;
   constexpr int CPR = D / 8;                   // 16-byte chunks per row
   constexpr int TILE = BC * D;                 // bf16 elements per K or V tile
@@ -182,41 +182,114 @@ void prefill_kernel(PrefillArgs a) {
     qf[kk] = as_bf16x8(x);
   }
 
-  // Visit list: dense (ascending tiles up to the causal limit) or a block list.
-  const int32_t* list = nullptr;
-  int n_list;
+  // Visit sequence: (tile j, mask of the units that visit it), j = -1 at the
+  // end. Dense: ascending tiles up to the causal limit, every unit (a unit
+  // whose rows cannot see a tile skips its vote through uvis below). Block
+  // lists: each unit visits the valid entries of its own list in list order.
+  // With two units per workgroup (64-row units of a block list) the two
+  // lists are merged by tile index when both are ascending -- a tile on both
+  // lists is visited once for both, and each unit still sees its own tiles
+  // in its own order -- and otherwise visited one after the other.
+  constexpr int kEnd = 0x7fffffff;
+  int cur_t = 0;  // dense cursor
+  const int n_dense = a.causal ? (last_row / BC + 1) : a.nK;
+  const int32_t* lp[NU];
+  int nl[NU], ulim[NU], pos[NU], head[NU], cbase[NU], cval[NU];
+  bool merge = true;
   if (SPARSE) {
-    list = a.block_idx + unit * a.max_blocks;
-    n_list = min(max(a.block_cnt[unit], 0), a.max_blocks);
-  } else {
-    n_list = a.causal ? (last_row / BC + 1) : a.nK;
+#pragma unroll
+    for (int uu = 0; uu < NU; ++uu) {
+      const size_t uid = (size_t)(b * a.Hq + hq) * a.nQ_unit + (size_t)i * NU + uu;
+      const bool exists = i * NU + uu < a.nQ_unit;
+      lp[uu] = a.block_idx + (exists ? uid : 0) * a.max_blocks;
+      nl[uu] = exists ? min(max(a.block_cnt[uid], 0), a.max_blocks) : 0;
+      ulim[uu] = min(q0 + (uu + 1) * UW * 32 - 1, L - 1);
+      pos[uu] = 0;
+      cbase[uu] = -64;
+      cval[uu] = 0;
+    }
   }
   // A block list is read 64 entries at a time, one per lane, and entry t is
   // taken from lane t % 64: one vector load per 64 tiles instead of a load
   // (and a wait behind the tile loads in flight) per tile.
-  int lst_base = -64, lst_val = 0;
-  auto list_at = [&](int t) -> int {
+  auto entry = [&](int uu, int t) -> int {
     const int blk = t & ~63;
-    if (blk != lst_base) {
-      lst_base = blk;
-      lst_val = blk + lane < n_list ? list[blk + lane] : -1;
+    if (blk != cbase[uu]) {
+      cbase[uu] = blk;
+      cval[uu] = blk + lane < nl[uu] ? lp[uu][blk + lane] : -1;
     }
-    return __builtin_amdgcn_readlane(lst_val, t & 63);
+    return __builtin_amdgcn_readlane(cval[uu], t & 63);
   };
-  auto valid = [&](int j) -> bool {
-    return j >= 0 && j < a.nK && (!a.causal || j * BC <= last_row);
+  auto valid_u = [&](int uu, int j) -> bool {
+    return j >= 0 && j < a.nK && (!a.causal || j * BC <= ulim[uu]);
   };
-  // First valid list position >= t (n_list if none) and its tile j.
-  auto advance = [&](int t, int& j) -> int {
+  // head[uu]: the tile at the first valid position >= pos[uu] (kEnd if none).
+  auto seek = [&](int uu) {
+    for (; pos[uu] < nl[uu]; ++pos[uu]) {
+      const int j = entry(uu, pos[uu]);
+      if (valid_u(uu, j)) {
+        head[uu] = j;
+        return;
+      }
+    }
+    head[uu] = kEnd;
+  };
+  if (SPARSE) {
+#pragma unroll
+    for (int uu = 0; uu < NU; ++uu) {
+      if (NU > 1) {
+        // strictly ascending valid entries? (each valid entry above the
+        // largest valid entry before it: a prefix max across the lanes)
+        int before = -1;
+        for (int t0 = 0; t0 < nl[uu]; t0 += 64) {
+          const int j = t0 + lane < nl[uu] ? lp[uu][t0 + lane] : -1;
+          const bool v = valid_u(uu, j);
+          int pm = v ? j : -1;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(pm, o, kWave);
+            if (lane >= o) pm = max(pm, y);
+          }
+          int ex = __shfl_up(pm, 1, kWave);
+          ex = max(lane == 0 ? -1 : ex, before);
+          if (__ballot(v && j <= ex) != 0ull) merge = false;
+          before = max(before, __shfl(pm, 63, kWave));
+        }
+      }
+      seek(uu);
+    }
+  }
+  auto next_tile = [&](int& j, int& m) {
     if (!SPARSE) {
-      j = t;
-      return t;
+      j = cur_t < n_dense ? cur_t++ : -1;
+      m = (1 << NU) - 1;
+      return;
     }
-    for (; t < n_list; ++t) {
-      j = list_at(t);
-      if (valid(j)) break;
+    if (NU == 1) {
+      j = head[0] == kEnd ? -1 : head[0];
+      m = 1;
+      if (j >= 0) {
+        ++pos[0];
+        seek(0);
+      }
+      return;
     }
-    return t;
+    const int h0 = head[0], h1 = head[NU - 1];
+    if (merge) {
+      const int jm = min(h0, h1);
+      j = jm == kEnd ? -1 : jm;
+      m = (h0 == jm ? 1 : 0) | (h1 == jm ? 2 : 0);
+      if (j < 0) m = 0;
+    } else {
+      j = h0 != kEnd ? h0 : (h1 != kEnd ? h1 : -1);
+      m = j < 0 ? 0 : (h0 != kEnd ? 1 : 2);
+    }
+#pragma unroll
+    for (int uu = 0; uu < NU; ++uu)
+      if ((m >> uu) & 1) {
+        ++pos[uu];
+        seek(uu);
+      }
   };
 
   // LDS-direct tile loads: this wave fills LPW consecutive 1 KiB blocks; LDS
@@ -261,6 +334,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) p[c] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   int vpar = 0;
+  bool pend = false;  // 32-row units: this wave's P awaits its P.V
 #pragma unroll
   for (int x = tid; x < TILE / 8; x += NT) store16(v_lds[0] + x * 8, u32x4{0u, 0u, 0u, 0u});
   int skipped = 0;
@@ -376,11 +450,12 @@ void prefill_kernel(PrefillArgs a) {
       }
   };
 
-  int jcur = 0, jnext = 0;  // tiles at list positions tcur and tnext
-  int tcur = advance(0, jcur);
-  if (tcur < n_list) load_tile(kp, jcur, k_lds0, koff);
-  int tnext = tcur < n_list ? advance(tcur + 1, jnext) : n_list;
-  int jprev = -1;  // tile of the previous position
+  // tiles (and unit masks) of the current, next and previous positions
+  int jcur, mcur, jnext, mnext;
+  next_tile(jcur, mcur);
+  if (jcur >= 0) load_tile(kp, jcur, k_lds0, koff);
+  next_tile(jnext, mnext);
+  int jprev = -1, mprev = 0;
   // One pipeline step per list position t (the loop runs t = 0 .. n, one
   // barrier each): vote of tile t-1; if kept, P.V of the previous kept tile
   // with the exponentials of tile t-1 and the K(t+1) loads, then V(t-1);
@@ -390,7 +465,7 @@ void prefill_kernel(PrefillArgs a) {
     constexpr int buf = decltype(buf_c)::value;
     uint16_t* const k_cur = buf == 0 ? k_lds0 : k_lds1;  // K(t), read by the scores
     uint16_t* const k_nxt = buf == 0 ? k_lds1 : k_lds0;  // K(t+1), loaded now
-    const bool have_cur = tcur < n_list;
+    const bool have_cur = jcur >= 0;
     const bool have_prev = jprev >= 0;
     if (!have_cur && !have_prev) return false;
     // K(t) and the last kept V (LDS-direct loads) and the flags of tile t-1
@@ -403,8 +478,10 @@ void prefill_kernel(PrefillArgs a) {
     if (have_prev) {
       // keep1: some decision unit of the workgroup keeps the tile;
       // keep_mine: this wave's unit keeps it. A unit whose rows cannot see
-      // the tile (causal) does not count it as visited.
-      const bool uvis = unit_rows && (!a.causal || jprev * BC <= unit_last);
+      // the tile (causal), or whose list does not hold it, does not count it
+      // as visited.
+      const bool uvis = SPARSE ? (((mprev >> u) & 1) != 0)
+                               : (unit_rows && (!a.causal || jprev * BC <= unit_last));
       if (STATS) {
         float gu = flag_lds[buf ^ 1][u * UW];
 #pragma unroll
@@ -469,7 +546,7 @@ void prefill_kernel(PrefillArgs a) {
       // queue while the matrix cores work. Past the last position the
       // resource is empty and the loads write zeros into the free buffer
       // (no branch splits the block).
-      const bool kn = tnext < n_list;
+      const bool kn = jnext >= 0;
       const int kb0n = kn ? jnext * BC : 0;
       const auto rsk = make_rsrc(kp + (size_t)kb0n * D, kn ? min(L - kb0n, BC) * D * 2 : 0);
       auto k_share = [&](int c) __attribute__((always_inline)) {
@@ -477,13 +554,29 @@ void prefill_kernel(PrefillArgs a) {
         for (int r = 0; r < LPW; ++r)
           if (r * 4 / LPW == c) load_lds16_buf(rsk, koff[r], k_nxt + (wu * LPW + r) * 512);
       };
-      pv_chunk(vt, 0);
-      k_share(0);
+      if constexpr (UW == 1) {
+        // Every wave is a decision unit of its own (32-row units): the P.V
+        // of its pending P runs only if its unit kept the last kept tile,
+        // and the exponentials only if its unit keeps this one (branches
+        // uniform per wave), so the matrix and exponential work follow the
+        // unit's own decisions; the V tile is still shared.
+        if (pend) pv_chunk(vt, 0);
+        k_share(0);
 #pragma unroll
-      for (int c = 0; c < 3; ++c) {
-        pv_chunk(vt, c + 1);
-        k_share(c + 1);
-        exp_chunk(c, mc, psum);
+        for (int c = 0; c < 3; ++c) {
+          if (pend) pv_chunk(vt, c + 1);
+          k_share(c + 1);
+          if (keep_mine) exp_chunk(c, mc, psum);
+        }
+      } else {
+        pv_chunk(vt, 0);
+        k_share(0);
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+          pv_chunk(vt, c + 1);
+          k_share(c + 1);
+          exp_chunk(c, mc, psum);
+        }
       }
       if constexpr (VSINGLE) {
         // Every wave is done reading the V buffer before any wave loads
@@ -503,9 +596,10 @@ void prefill_kernel(PrefillArgs a) {
       // not used) overlap the last exponential chunk: keys 0..31 go to s[0],
       // already consumed, while chunk 3 reads s[1].
       scores_half(k_cur, 0);
-      exp_chunk(3, mc, psum);
+      if (UW > 1 || keep_mine) exp_chunk(3, mc, psum);
       scores_half(k_cur, 1);
       l_acc += psum;
+      if constexpr (UW == 1) pend = keep_mine;
     }
     if (have_cur && !keep1) {
 #pragma unroll
@@ -523,7 +617,7 @@ void prefill_kernel(PrefillArgs a) {
     // Without a kept tile, K(t+1) is issued after the scores of tile t: the
     // loads queue behind the other waves' loads while the matrix cores work
     // (measured ~1% faster than issuing them right after the vote).
-    if (!keep1 && tnext < n_list) load_tile(kp, jnext, k_nxt, koff);
+    if (!keep1 && jnext >= 0) load_tile(kp, jnext, k_nxt, koff);
     jprev = -1;
     if (have_cur) {
       const int j = jcur;
@@ -541,6 +635,13 @@ void prefill_kernel(PrefillArgs a) {
             if (kb * 32 + (e >> 2) * 8 + (e & 3) > lim) s[kb][e] = -INFINITY;
       }
       if (NM) nm_sparsify(kbase);
+      if (SPARSE && NU > 1 && ((mcur >> u) & 1) == 0) {
+        // the tile is on the other unit's list only: no score of this unit
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[kb][e] = -INFINITY;
+      }
       float mloc = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -560,9 +661,10 @@ void prefill_kernel(PrefillArgs a) {
       }
       m_run = fmaxf(m_run, mloc);
       jprev = j;
-      tcur = tnext;
+      mprev = mcur;
       jcur = jnext;
-      tnext = tcur < n_list ? advance(tcur + 1, jnext) : n_list;
+      mcur = mnext;
+      next_tile(jnext, mnext);
     }
     return true;
   };
@@ -571,8 +673,10 @@ void prefill_kernel(PrefillArgs a) {
   // P.V of the last kept tile (of zeros if none was kept).
   wait_vmem_lds();
   __syncthreads();
+  if (UW > 1 || pend) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) pv_chunk(v_lds[VSINGLE ? 0 : vpar], c);
+    for (int c = 0; c < 4; ++c) pv_chunk(v_lds[VSINGLE ? 0 : vpar], c);
+  }
 
   // Epilogue: normalise, write out (bf16) and lse.
   const float l_tot = sum_halves(l_acc);
@@ -604,7 +708,7 @@ hipError_t launch(const PrefillArgs& a, hipStream_t stream) {
 #define SSA_LAUNCH(ST, SP, NMF) \
   hipLaunchKernelGGL((prefill_kernel<D, BR, ST, SP, NMF, UW>), grid, block, 0, stream, a)
   if (a.block_idx != nullptr) {
-    if constexpr (BR / 32 == UW) {
+    if constexpr (BR / 32 == UW || (BR == 128 && UW == 2)) {
       if (stats) SSA_LAUNCH(true, true, false);
       else SSA_LAUNCH(false, true, false);
     } else {
@@ -638,11 +742,14 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   a.Hkv = p.Hkv;
   a.L = p.L;
   // Workgroup rows: Br = 32 units run four to a 128-row workgroup (per-wave
-  // votes); at d = 128 without a block list, Br = 64 units run two to a
-  // 128-row workgroup (a 64-row workgroup holds the same 64 KiB of K/V
-  // tiles, so only one of its waves would fit per SIMD); otherwise one unit
-  // per workgroup.
-  const bool pair64 = p.Br == 64 && p.d == 128 && p.block_idx == nullptr;
+  // votes); at d = 128, Br = 64 units run two to a 128-row workgroup (a
+  // 64-row workgroup holds the same 64 KiB of K/V tiles, so only one of its
+  // waves would fit per SIMD; with block lists the two lists are merged, so
+  // a tile on both is loaded once for 128 rows); otherwise one unit per
+  // workgroup. (At d = 64 the 64-row workgroups with one V buffer fit six
+  // to a CU, and pairing their block lists measured 12-27% slower on the
+  // 32K block-sparse legs.)
+  const bool pair64 = p.Br == 64 && p.d == 128;
   const int br_wg = (p.Br == 32 || pair64) ? 128 : p.Br;
   a.nQ = (p.L + br_wg - 1) / br_wg;
   a.nQ_unit = (p.L + p.Br - 1) / p.Br;
@@ -675,7 +782,7 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
     if (p.d == 128) return launch<128, 128, 4>(a, stream);
     if (p.d == 64) return launch<64, 128, 4>(a, stream);
   } else if (p.Br == 64) {
-    if (p.d == 128) return pair64 ? launch<128, 128, 2>(a, stream) : launch<128, 64, 2>(a, stream);
+    if (p.d == 128) return launch<128, 128, 2>(a, stream);
     if (p.d == 64) return launch<64, 64, 2>(a, stream);
   }
   return hipErrorInvalidValue;

@@ -164,3 +164,70 @@ def test_block_list_any_order(d, Br):
         print(f"d={d} lambda={lam:.3f}: skipped {r['skipped']}/{r['visited']}")
         if lam > -math.inf:
             assert r["skipped"] > 0
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_block_lists_of_paired_units(d):
+    """64-row units with block lists run two to a 128-row workgroup, their
+    lists merged when both are ascending and visited one after the other
+    otherwise: ascending pairs, pairs with one shuffled list, disjoint lists,
+    entries valid for one unit of the pair only (causal), an empty list, and
+    an odd number of units (the last workgroup holds one)."""
+    L = 64 * 13 + 5
+    q, k, v = _inputs(208, d, 1, 3, 1, L, d)
+    nQ = math.ceil(L / 64)
+    rng = np.random.default_rng(5)
+    mb = 20
+    idx = np.full((1, 3, nQ, mb), -1, np.int32)
+    cnt = np.zeros((1, 3, nQ), np.int32)
+    for h in range(3):
+        for i in range(nQ):
+            if h == 2 and i % 4 == 1:
+                continue                                  # empty list
+            pool = list(range(i + 1))
+            if h == 1:
+                pool = [j for j in pool if (j + i) % 2 == 0] or [i]   # neighbours share few tiles
+            keep = sorted(rng.choice(pool, size=min(len(pool), int(rng.integers(1, 9))), replace=False).tolist())
+            if i % 2 == 0 and i + 1 < nQ:
+                keep.append(i + 1)                        # above this unit's causal limit: ignored
+            if h == 0 and i % 6 == 3:
+                rng.shuffle(keep)                         # one list of the pair not ascending
+            idx[0, h, i, :len(keep)] = keep
+            cnt[0, h, i] = len(keep)
+    for lam in (-math.inf, -0.5):
+        r = prefill_parity(q, k, v, lam, 64, 64, True, block_idx=idx, block_cnt=cnt)
+        print(f"d={d} lambda={lam}: skipped {r['skipped']}/{r['visited']} exempt {r['exempt']}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_block_list_with_repeated_entries(d):
+    # a repeated entry is visited again (its keys count twice), in the
+    # kernel as in the oracle; with Br = 64 such a list is not strictly
+    # ascending, so the two lists of a workgroup are visited one after the
+    # other. Skip counts count visits, so they are compared with the
+    # oracle's directly (per-tile arrays keep the last visit).
+    import torch
+    import sparse_attention_long_skip_amd as ssa
+    from parity import dev_bf16, to_np, assert_close, BAND
+    L = 64 * 9
+    q, k, v = _inputs(209, d, 1, 2, 1, L, d)
+    nQ = L // 64
+    idx = np.full((1, 2, nQ, 12), -1, np.int32)
+    cnt = np.zeros((1, 2, nQ), np.int32)
+    for h in range(2):
+        for i in range(nQ):
+            lst = [0, i, i // 2, i] if h == 0 else [i // 3, i // 3, i]
+            idx[0, h, i, :len(lst)] = lst
+            cnt[0, h, i] = len(lst)
+    bi, bc = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    for lam in (-math.inf, -1.0):
+        ref = oracle.prefill(q, k, v, lam, 64, 64, True, block_idx=idx, block_cnt=cnt, bits=True)
+        near = np.abs(ref["margin"] - lam) < BAND
+        assert not near.any()
+        for kw in (dict(stats=True), dict(counts=True)):
+            g = ssa.prefill(qd, kd, vd, lam, Br=64, Bc=64, causal=True, block_idx=bi, block_cnt=bc, **kw)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(to_np(g["skip_counts"]), ref["skip_counts"])
+            assert_close("out", to_np(g["out"]), ref["out"])
+            assert_close("lse", to_np(g["lse"]), ref["lse"], rtol_l2=1.0)
