@@ -79,3 +79,12 @@ def test_split_boundaries_24(lens):
         r = decode_parity(y, lam, 24)
         print(f"lens={lens} lambda={lam}: skipped {r['skipped']}/{r['visited']}")
 
+
+@pytest.mark.parametrize("lens", [[1023, 1024, 1025, 2048], [64 * 16 * 3 - 1, 1, 64 * 16 + 63, 4100]])
+def test_split_boundaries_16(lens):
+    # splits of 16 tiles (1024 keys, the benchmarked split length): lengths at
+    # and around split ends; four query heads per KV head
+    y = synth.decode_inputs(305, len(lens), len(lens), 8, 2, 4608, 128, 1, 4608, seqlens=lens)
+    for lam in (-math.inf, -0.4):
+        r = decode_parity(y, lam, 16)
+        print(f"lens={lens} lambda={lam}: skipped {r['skipped']}/{r['visited']}")
