@@ -123,7 +123,8 @@ int ssa_prefill_nm(const void* q, const void* k, const void* v, void* out, float
 /*
  * ssa_decode_workspace_size -- bytes of device workspace ssa_decode needs:
  * per (sequence, query head, split) one fp32 partial output of d values plus
- * its running max and row-sum. Returns 0 for invalid sizes.
+ * its running max and row-sum, then a 256-byte block holding the split
+ * kernel's work counter. Returns 0 for invalid sizes.
  */
 size_t ssa_decode_workspace_size(int B, int Hq, int S_max, int d, int Bc, int split_tiles);
 
@@ -148,7 +149,10 @@ size_t ssa_decode_workspace_size(int B, int Hq, int S_max, int d, int Bc, int sp
  *  restarts the running max, so its first tile is always kept.
  *  d in {64, 128}; Bc = 64; G in {1, 2, 4, 8, 16}; split_tiles >= 1.
  *  workspace: device buffer of at least ssa_decode_workspace_size(...) bytes,
- *           4-byte aligned; its contents on entry are ignored.
+ *           16-byte aligned; its contents on entry are ignored (the call
+ *           sets the work counter itself, with a kernel, before the split
+ *           kernel runs).
+ *  Calls with B * Hkv * nS >= 2^31 return SSA_ERR_UNSUPPORTED.
  */
 int ssa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
                void* out, float* lse, int32_t* skip_counts, uint8_t* tile_state,
@@ -175,7 +179,8 @@ int ssa_decode(const void* q, const void* k_cache, const void* v_cache, const in
  *  - All calls on one GPU share that GPU's scratch: calls that overlap on a
  *    GPU (different streams, or host threads without ordering) race. Calls
  *    ordered on one stream are safe. No scratch content needs to start at
- *    zero: every partial the combine reads is written by the same call.
+ *    zero: every partial the combine reads is written by the same call, and
+ *    the call sets the work counter (with a kernel) before it is used.
  */
 int ssa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
                        void* out, float* lse, int32_t* skip_counts, uint8_t* tile_state,

@@ -25,6 +25,14 @@ FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
 ]
 
+# Per-source extra flags. decode.hip: the split kernel takes a work ticket
+# with one atomic add from lane 0 and reads the result a tile later; the
+# compiler's atomic optimizer would rewrite it into a wave-aggregated add
+# whose result is waited for at once.
+EXTRA_FLAGS = {
+    "decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+}
+
 
 def build(verbose: bool = False, jobs: int = 4, lib_path: str = LIB, overrides: dict | None = None,
           objdir: str | None = None) -> str:
@@ -44,7 +52,7 @@ def build(verbose: bool = False, jobs: int = 4, lib_path: str = LIB, overrides: 
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
         path = overrides.get(src, os.path.join(CSRC, src))
-        cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, *lang, "-c", path, "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, *lang, "-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))

@@ -146,6 +146,14 @@ __device__ __forceinline__ uint64_t lds_read_tr16(const void* lds_addr) {
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// 16-byte buffer load at byte offset voff: zero when the chunk lies at or
+// past the resource's end. Only the vector and immediate offsets take part
+// in that range check (a scalar offset would not), so the whole offset
+// goes in voff.
+__device__ __forceinline__ u32x4 load16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)voff, 0, 0));
+}
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 }  // namespace ssa

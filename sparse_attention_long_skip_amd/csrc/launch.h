@@ -131,15 +131,19 @@ hipError_t decode_scratch(void** ptr);
 hipError_t launch_lambda_for_ratio(const float* margins, long long n, double target, double window,
                                    double* result, void* workspace, hipStream_t stream);
 
-// Decode workspace layout: partial o [B, Hq, nS, d] fp32, then (m, l) [B, Hq, nS, 2] fp32.
+// Decode workspace layout: partial o [B, Hq, nS, d] fp32, then (m, l)
+// [B, Hq, nS, 2] fp32, then a 256-byte block whose first word is the split
+// kernel's work counter.
 inline size_t decode_num_splits(int S_max, int Bc, int split_tiles) {
   size_t nT = ((size_t)S_max + Bc - 1) / Bc;
   return (nT + split_tiles - 1) / split_tiles;
 }
 
+constexpr size_t kDecodeQueueBytes = 256;
+
 inline size_t decode_workspace_bytes(int B, int Hq, int S_max, int d, int Bc, int split_tiles) {
   size_t nS = decode_num_splits(S_max, Bc, split_tiles);
-  return (size_t)B * Hq * nS * ((size_t)d + 2) * sizeof(float);
+  return (size_t)B * Hq * nS * ((size_t)d + 2) * sizeof(float) + kDecodeQueueBytes;
 }
 
 inline size_t mask_workspace_bytes(int B, int H, int L, int d, int pool) {

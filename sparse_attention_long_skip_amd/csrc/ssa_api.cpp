@@ -72,6 +72,8 @@ int check_decode(const void* q, const void* kc, const void* vc, const int32_t* s
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return SSA_ERR_UNSUPPORTED;
   const size_t nS = ssa::decode_num_splits(S_max, Bc, split_tiles);
   if (nS > 65535 || Hkv > 65535 || B > 65535 || Hq > 65535) return SSA_ERR_UNSUPPORTED;
+  // splits are numbered by a 32-bit work counter
+  if ((long long)B * Hkv * (long long)nS >= (1ll << 31)) return SSA_ERR_UNSUPPORTED;
   if (!ws || !aligned(ws, 16)) return SSA_ERR_WORKSPACE;
   if (ws_bytes < ssa::decode_workspace_bytes(B, Hq, S_max, d, Bc, split_tiles))
     return SSA_ERR_WORKSPACE;

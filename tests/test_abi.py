@@ -43,7 +43,8 @@ def test_status_strings_and_helpers(lib):
     assert math.isnan(ssa.lambda_from_scale_factor(-1.0, 10))
     assert ssa.block_mask_max_blocks(32768, 64, 64, 1, 1024) == 81
     assert ssa.block_mask_max_blocks(1000, 64, 64, 1, 1024) == 16
-    assert ssa.decode_workspace_size(32, 32, 32768, 128, 64, 32) == 32 * 32 * 16 * 130 * 4
+    # partials, then the 256-byte block of the work counter
+    assert ssa.decode_workspace_size(32, 32, 32768, 128, 64, 32) == 32 * 32 * 16 * 130 * 4 + 256
     assert ssa.decode_workspace_size(0, 32, 32768, 128, 64, 32) == 0
 
 
