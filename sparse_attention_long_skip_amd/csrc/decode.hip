@@ -354,56 +354,75 @@ void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// One workgroup per (query head, sequence) merges the split partials in one
-// pass: thread t (< D) keeps the log-sum-exp of the splits seen so far and
-// the output element t weighted against it, rescaling both when a split
-// raises the maximum; the partials are read 16 splits per batch of loads
-// (every load issued before the first use).
+// One wave per (query head, sequence) merges the split partials, 64 splits
+// per batch: lane s holds split s's log-sum-exp lse_s = m_s / sqrt(d) +
+// ln l_s (splits with l_s = 0 hold no kept key and are left out); with
+// top = max lse_s, tot = sum exp(lse_s - top) and out = sum exp(m_s /
+// sqrt(d) - top) o_s / tot, lse = top + ln tot. A lane owns D / 64 output
+// elements; a batch's partial loads are all issued before the first use,
+// and each split's weight reaches every lane by a scalar read.
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
-  constexpr int U = 16;
+__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int E = D / kWave;  // output elements per lane
+  constexpr int U = 32;         // partial rows in flight per lane
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
-  const int t = threadIdx.x;
+  const int lane = threadIdx.x;
   const int n = min(max(a.seqlens[b], 0), a.S_max);
   const int ntiles = (n + BC - 1) / BC;
   const int nsp = (ntiles + a.T - 1) / a.T;
   const size_t base = ((size_t)b * a.Hq + hq) * a.nS;
-  // lse_s = m_s / sqrt(d) + ln l_s over the splits with l_s > 0;
-  // top = max lse_s, tot = sum exp(lse_s - top),
-  // acc = sum exp(m_s / sqrt(d) - top) o_s[t].
-  float top = -INFINITY, tot = 0.f, acc = 0.f;
-  for (int s0 = 0; s0 < nsp; s0 += U) {
-    float mm[U], ll[U], oo[U];
+  float top = -INFINITY, tot = 0.f;
+  float acc[E];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool ok = s0 + u < nsp;
-      mm[u] = ok ? a.ws_ml[(base + s0 + u) * 2] : 0.f;
-      ll[u] = ok ? a.ws_ml[(base + s0 + u) * 2 + 1] : 0.f;
-      oo[u] = ok ? a.ws_o[(base + s0 + u) * D + t] : 0.f;
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int s0 = 0; s0 < nsp; s0 += kWave) {
+    const int s = s0 + lane;
+    float x = -INFINITY, ms = -INFINITY;
+    if (s < nsp) {
+      const float m = a.ws_ml[(base + s) * 2];
+      const float l = a.ws_ml[(base + s) * 2 + 1];
+      if (l > 0.f) {
+        ms = m * a.inv_sqrt_d;
+        x = ms + __logf(l);
+      }
     }
+    const float bt = wave_max(x);
+    if (bt > top) {
+      // rescale what the earlier batches summed (nothing if top = -inf)
+      const float sc = __expf(top - bt);
+      tot *= sc;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (ll[u] > 0.f) {
-        const float ms = mm[u] * a.inv_sqrt_d;
-        const float x = ms + __logf(ll[u]);
-        if (x > top) {
-          const float sc = __expf(top - x);
-          tot = tot * sc + 1.f;
-          acc = acc * sc + __expf(ms - x) * oo[u];
-          top = x;
-        } else {
-          tot += __expf(x - top);
-          acc += __expf(ms - top) * oo[u];
-        }
+      for (int e = 0; e < E; ++e) acc[e] *= sc;
+      top = bt;
+    }
+    if (top == -INFINITY) continue;  // no kept key so far
+    tot += wave_sum(x == -INFINITY ? 0.f : __expf(x - top));
+    const float wo = ms == -INFINITY ? 0.f : __expf(ms - top);
+    const int cnt = min(kWave, nsp - s0);
+    for (int u0 = 0; u0 < cnt; u0 += U) {
+      float oo[U][E];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          oo[u][e] = u0 + u < cnt ? a.ws_o[(base + s0 + u0 + u) * D + e * kWave + lane] : 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float w = __builtin_amdgcn_readlane(__float_as_int(wo), (u0 + u) & (kWave - 1));
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(__int_as_float(w), oo[u][e], acc[e]);
       }
     }
   }
   const float lse = (tot > 0.f) ? top + __logf(tot) : -INFINITY;
-  const float r = tot > 0.f ? acc / tot : 0.f;
-  const __bf16 rb = (__bf16)r;
-  a.out[((size_t)b * a.Hq + hq) * D + t] = __builtin_bit_cast(uint16_t, rb);
-  if (a.lse && t == 0) a.lse[(size_t)b * a.Hq + hq] = lse;
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const __bf16 rb = (__bf16)(acc[e] * inv);
+    a.out[((size_t)b * a.Hq + hq) * D + e * kWave + lane] = __builtin_bit_cast(uint16_t, rb);
+  }
+  if (a.lse && lane == 0) a.lse[(size_t)b * a.Hq + hq] = lse;
 }
 
 // The split kernel's work counter is set before every launch (a kernel, not
@@ -444,7 +463,7 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(a.Hq, a.B);
-  hipLaunchKernelGGL((decode_combine_kernel<D>), g2, dim3(D), 0, stream, a);
+  hipLaunchKernelGGL((decode_combine_kernel<D>), g2, dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }
 
