@@ -94,6 +94,10 @@ def test_decode_validation(lib):
     assert _decode(lib, d=80) == -2
     assert _decode(lib, ws=None) == -3
     assert _decode(lib, wsb=16) == -3
+    # splits are numbered by a 32-bit work counter: B * Hkv * nS < 2^31
+    # (4096 * 512 * 1024 = 2^31 splits with S_max = 65536, one-tile splits)
+    assert _decode(lib, B=4096, Hq=512, Hkv=512, S=65536, T=1) == -2
+    assert _decode(lib, B=4095, Hq=512, Hkv=512, S=65536, T=1) == -3   # fits; workspace too small
 
 
 def _decode_noalloc(lib, **kw):
