@@ -274,8 +274,6 @@ void decode_split_kernel(DecodeArgs a) {
       else if (m_prev == -INFINITY) gap = INFINITY;
       else gap = mloc - m_prev;
       const float gw = wave_max(gap);
-      // (uniform by construction; said so, so that the branch is scalar and
-      // the values this loop hands to the next item stay scalar)
       const bool skip = gw < a.lam_raw;
       if (lane == 0) {
         const size_t ti = ((size_t)b * a.Hkv + kvh) * a.nT + j;

@@ -88,3 +88,41 @@ def test_split_boundaries_16(lens):
     for lam in (-math.inf, -0.4):
         r = decode_parity(y, lam, 16)
         print(f"lens={lens} lambda={lam}: skipped {r['skipped']}/{r['visited']}")
+
+
+def test_work_queue_sparse_tickets_and_reuse():
+    # The split kernel hands out (sequence, KV head, split) tickets from a work
+    # counter. Here a third of the sequences are empty and a third hold under
+    # two tiles, so most tickets fall past a sequence's end and the counter
+    # jumps; 48 * 4 * 32 = 6144 tickets for 1024 waves. Two calls on one
+    # workspace (the counter is set by each call), the second with fewer
+    # sequences and shorter lengths (rows past the first call's lengths are
+    # NaN in these caches).
+    import torch
+    import sparse_attention_long_skip_amd as ssa
+    from parity import dev_bf16
+    rng = np.random.default_rng(306)
+    B, S = 48, 4096
+    i = np.arange(B)
+    lens = np.where(i % 3 == 0, 0, np.where(i % 3 == 1, rng.integers(1, 128, B), rng.integers(1000, S + 1, B)))
+    y = synth.decode_inputs(306, 0, B, 8, 4, S, 128, 1, S, seqlens=lens)
+    r = decode_parity(y, -0.5, 2)
+    print(f"skipped {r['skipped']}/{r['visited']}")
+    ws = torch.empty(ssa.decode_workspace_size(B, 8, S, 128, 64, 2), dtype=torch.uint8, device="cuda")
+    q, kc, vc = dev_bf16(y["q"]), dev_bf16(y["k_cache"]), dev_bf16(y["v_cache"])
+    for call, lens_c in enumerate((lens, lens[:40] // 2)):
+        Bc = len(lens_c)
+        seq = torch.tensor(lens_c, dtype=torch.int32, device="cuda")
+        g = ssa.decode(q[:Bc], kc[:Bc], vc[:Bc], seq, -0.5, split_tiles=2, workspace=ws, counts=True)
+        torch.cuda.synchronize()
+        ref = oracle.decode(y["q"][:Bc], y["k_cache"][:Bc], y["v_cache"][:Bc], lens_c, -0.5, 64, 2,
+                            bits=True)
+        out = g["out"].float().cpu().numpy()
+        assert np.all(np.isfinite(out)) and np.all(np.isfinite(ref["out"])), f"call {call}"
+        assert np.abs(out - ref["out"]).max() < 2e-2, f"call {call}"
+        sc = g["skip_counts"].cpu().numpy()
+        # splits past the end of a sequence report 0; the rest within the band
+        for b in range(Bc):
+            nsp = -(-(-(-int(lens_c[b]) // 64)) // 2)
+            assert np.all(sc[b, :, nsp:] == 0)
+        assert abs(int(sc.sum()) - int(ref["skip_counts"].sum())) <= max(2, int(0.01 * ref["skip_counts"].sum()))
