@@ -9,20 +9,20 @@
 //
 // Design: each split (sequence, KV head, split) is run by one wave, so the
 // vote and the softmax never need a workgroup barrier. The split kernel is
-// persistent: one wave per resident wave slot takes splits from a work
-// counter in split-major order (every first split, then every second one,
-// ...: the short last splits come at the end) and, during the last tile of
-// a split, already loads the query rows and first K tile of its next one.
-// A wave slot thus never waits for a new wave to be dispatched and for its
-// first loads to arrive, which with one wave per split cost about a fifth
-// of the slot time. Scores use 16x16x32 bf16 MFMA (S^T = K Q^T, K rows read
+// persistent: three waves per CU take splits from a work counter in
+// (sequence, KV head, split) order and, during the last tile of a split,
+// already loads the query rows and first K tile of its next one. A wave
+// slot thus never waits for a new wave to be dispatched and for its first
+// loads to arrive, which with one wave per split cost about a fifth of the
+// slot time. Scores use 16x16x32 bf16 MFMA (S^T = K Q^T, K rows read
 // straight from HBM as the A operand, the G query rows as B-operand
 // columns). The K tile for step j+1 is prefetched into registers while step
 // j runs; the V tile is issued only after the vote, and its P.V waits until
-// the scores and vote of the next tile are done. P.V runs on the vector
-// units: V rows are read with coalesced 16-byte loads (each row is 16 lanes
-// x 16 B at d = 128) and the probabilities come from a small per-wave LDS
-// table.
+// the scores and vote of the next tile are done. P.V also runs on 16x16x32
+// MFMA (O^T = V^T P^T): V rows arrive with coalesced 16-byte loads (each row
+// is 16 lanes x 16 B at d = 128), pass through a swizzled LDS tile and come
+// back through transposing reads as the A operand, while each lane's own
+// exponentials are its B operand.
 #include <algorithm>
 #include <atomic>
 #include <mutex>
@@ -66,10 +66,10 @@ struct DecodeArgs {
   float inv_sqrt_d;
 };
 
-// One wave per SIMD: the cache streams are read faster with fewer of them
-// in flight (on the 32-sequence, 16K-32K workload: 0.453 ms with one wave
-// per SIMD, 0.478 ms with two), and each wave may then use the whole
-// register file.
+// At most one wave per SIMD: the cache streams are read faster with fewer
+// of them in flight (on the 32-sequence, 16K-32K workload with vector P.V:
+// 0.453 ms with one wave per SIMD, 0.478 ms with two), and each wave may
+// then use the whole register file.
 template <int D, int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_split_kernel(DecodeArgs a) {
@@ -78,10 +78,10 @@ void decode_split_kernel(DecodeArgs a) {
   constexpr int RG = 64 / CPR;   // row groups across the wave
   constexpr int KPG = BC / RG;   // keys per row group and tile
 
-  // P and the rescale factor of a kept tile, double-buffered: the next kept
-  // tile's are written while the pending tile's P.V still reads them.
-  __shared__ __attribute__((aligned(16))) float p_lds[2][G][BC];
-  __shared__ float alpha_lds[2][G];
+  constexpr int NDB = D / 16;    // 16-row blocks of O^T (d) in the P.V products
+  // The V tile of the pending P.V, row-major with 16-byte chunks XOR-swizzled
+  // by row (chunk c of row r at c ^ (r % CPR)), read back transposed.
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[BC * D];
 
   const int lane = threadIdx.x;
   const int c16 = lane & 15;  // score column = query row g
@@ -174,11 +174,26 @@ void decode_split_kernel(DecodeArgs a) {
 
   const int rg = lane / CPR;
   const int cc = lane % CPR;
-  // V rows rg * KPG + m, chunk cc of a tile
+  // V rows rg * KPG + m, chunk cc of a tile (KPG = CPR, so row % CPR = m)
   const uint32_t v_off = (uint32_t)(rg * KPG * D + cc * 8) * 2u;
-  float o[G][8];
+  const int vw_base = rg * KPG * D;
+  // O^T += V^T P^T on 16x16x32 products: rows d (16 per block), columns the
+  // query rows g, reduction over the tile's keys, 32 per product. Reduction
+  // slot 8 q + t of k-step ks is key 32 ks + 16 (t / 4) + 4 q + t % 4: for
+  // the B operand (P^T) these are exactly the keys a lane's own scores hold
+  // (s[2 ks][t], s[2 ks + 1][t - 4]), and for the A operand (V^T) two
+  // transposing LDS reads of four rows each. Lane (q4, c16 = 4 e + j)
+  // addresses row 4 q4 + e (+ 32 ks + 16 h), columns 16 db + 4 j .. + 3, and
+  // receives column 16 db + c16 of those four rows.
+  const int tr_e = c16 >> 2, tr_j = c16 & 3;
+  const int tr_row = 4 * q4 + tr_e;
+  const int tr_sw = tr_row & (CPR - 1);
+  int trd[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+    trd[db] = tr_row * D + (((2 * db + (tr_j >> 1)) ^ tr_sw) * 8) + (tr_j & 1) * 4;
+  f32x4 oacc[NDB];  // O^T rows 16 db + 4 q4 + i, column (query row) c16
   u32x4 vreg[KPG];
-  int pb = 0;
 
   load_q(cur);
   load_k(a.kc + kv_base(cur), cur.n, cur.j0);
@@ -193,42 +208,36 @@ void decode_split_kernel(DecodeArgs a) {
     const uint16_t* vp = a.vc + kv_base(cur);
     const int hq0 = kvh * G;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_prev = -INFINITY;
     float l_acc = 0.f;
     int skipped = 0;
 
     // The V rows of a kept tile are loaded right after its vote, and its P.V
     // runs one step later, after the scores and the vote of the next tile:
-    // the V load has the next tile's matrix work to land behind.
-    bool pend = false;  // a kept tile awaits its P.V (V in vreg, P and alpha in LDS buffer pb)
+    // the V load has the next tile's matrix work to land behind. Its P (bf16
+    // B operands) and rescale factor wait in registers meanwhile.
+    bool pend = false;  // a kept tile awaits its P.V (V in vreg, P in p_pend)
+    bf16x8 p_pend[2];
+    float alpha_pend = 1.f;
     auto pv_pending = [&]() __attribute__((always_inline)) {
-      __syncthreads();
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float al = alpha_lds[pb][g];
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[g][e] *= al;
-      }
+        for (int i = 0; i < 4; ++i) oacc[db][i] *= alpha_pend;
+      // (one wave: its LDS accesses complete in order, so the reads below
+      // see these writes, and the writes follow the previous tile's reads)
 #pragma unroll
-      for (int m4 = 0; m4 < KPG; m4 += 4) {
+      for (int m = 0; m < KPG; ++m) store16(v_lds + vw_base + m * D + ((cc ^ m) * 8), vreg[m]);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const f32x4 pg = *reinterpret_cast<const f32x4*>(&p_lds[pb][g][rg * KPG + m4]);
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int mm = 0; mm < 4; ++mm) {
-            const u32x4 vv = vreg[m4 + mm];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-              o[g][2 * e2] = fmaf(pg[mm], bf16_lo(vv[e2]), o[g][2 * e2]);
-              o[g][2 * e2 + 1] = fmaf(pg[mm], bf16_hi(vv[e2]), o[g][2 * e2 + 1]);
-            }
-          }
+        for (int db = 0; db < NDB; ++db) {
+          const uint64_t lo = lds_read_tr16(v_lds + trd[db] + (32 * ks) * D);
+          const uint64_t hi = lds_read_tr16(v_lds + trd[db] + (32 * ks + 16) * D);
+          const u32x4 va = {(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+          oacc[db] = mfma16(as_bf16x8(va), p_pend[ks], oacc[db]);
         }
-      }
-      __syncthreads();
     };
 
     // During the last tile, after its scores, the next ticket is taken and
@@ -285,30 +294,36 @@ void decode_split_kernel(DecodeArgs a) {
         m_prev = fmaxf(m_prev, mloc);
         continue;
       }
-      // Exponentials of this tile into the other P buffer (the scores are then
-      // dead), the P.V of the pending tile, then this tile's V rows -- keys
-      // kbase + rg*KPG + m, d chunk cc -- into the registers it freed.
-      const int nb = pb ^ (pend ? 1 : 0);
+      // Exponentials of this tile (bf16 B operands, zero in the padding
+      // columns c16 >= G), the P.V of the pending tile, then this tile's V
+      // rows -- keys kbase + rg*KPG + m, d chunk cc -- into the registers
+      // it freed.
       const float m_new = fmaxf(m_prev, mloc);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = fast_exp2((m_prev - m_use) * a.c_log2);
       const float mc = m_use * a.c_log2;
       float psum = 0.f;
+      bf16x8 p_new[2];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        f32x4 pv;
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pv[e] = fast_exp2(fmaf(s[kb][e], a.c_log2, -mc));
-          psum += pv[e];
+        for (int t = 0; t < 8; t += 2) {
+          const f32x4& sk = s[2 * ks + t / 4];
+          float x0 = fast_exp2(fmaf(sk[t % 4], a.c_log2, -mc));
+          float x1 = fast_exp2(fmaf(sk[t % 4 + 1], a.c_log2, -mc));
+          if (c16 >= G) x0 = x1 = 0.f;
+          psum += x0 + x1;
+          w[t / 2] = cvt_pk_bf16(x0, x1);
         }
-        if (c16 < G) *reinterpret_cast<f32x4*>(&p_lds[nb][c16][kb * 16 + q4 * 4]) = pv;
+        p_new[ks] = as_bf16x8(w);
       }
       l_acc = l_acc * alpha + psum;
       m_prev = m_new;
-      if (lane < G) alpha_lds[nb][lane] = alpha;
       if (pend) pv_pending();
-      pb = nb;
+      p_pend[0] = p_new[0];
+      p_pend[1] = p_new[1];
+      alpha_pend = alpha;
       const auto rsv = wave_rsrc(vp + (size_t)kbase * D, max(0, min(n - kbase, BC)) * D * 2);
 #pragma unroll
       for (int m = 0; m < KPG; ++m) vreg[m] = load16_buf(rsv, v_off + m * D * 2);
@@ -316,25 +331,13 @@ void decode_split_kernel(DecodeArgs a) {
     }
     if (pend) pv_pending();
 
-    // Reduce o over the row groups (lanes with equal chunk index).
-#pragma unroll
-    for (int off = CPR; off < 64; off <<= 1)
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[g][e] += __shfl_xor(o[g][e], off, kWave);
     float l_tot = l_acc + __shfl_xor(l_acc, 16, kWave);
     l_tot += __shfl_xor(l_tot, 32, kWave);
     const size_t base = ((size_t)b * a.Hq + hq0) * a.nS + sp;
-    if (rg == 0) {
+    if (c16 < G) {
+      float* dst = a.ws_o + (base + (size_t)c16 * a.nS) * D + q4 * 4;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float* dst = a.ws_o + (base + (size_t)g * a.nS) * D + cc * 8;
-        f32x4 x0 = {o[g][0], o[g][1], o[g][2], o[g][3]};
-        f32x4 x1 = {o[g][4], o[g][5], o[g][6], o[g][7]};
-        *reinterpret_cast<f32x4*>(dst) = x0;
-        *reinterpret_cast<f32x4*>(dst + 4) = x1;
-      }
+      for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4*>(dst + db * 16) = oacc[db];
     }
     if (lane < G) {
       float* ml = a.ws_ml + (base + (size_t)lane * a.nS) * 2;
@@ -430,8 +433,10 @@ __global__ void decode_queue_reset(uint32_t* queue, uint32_t first) {
   if (threadIdx.x == 0) *queue = first;
 }
 
-// Waves of the persistent split kernel on the current device: one per SIMD
-// (four per CU), the CU count looked up once per device.
+// Waves of the persistent split kernel on the current device: three per CU
+// (fewer cache streams in flight read faster: with MFMA P.V on the
+// 32-sequence decode, 512 waves 0.445 ms, 640 0.441, 768 0.437, 1024
+// 0.440), the CU count looked up once per device.
 int split_waves() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev];
@@ -443,7 +448,7 @@ int split_waves() {
   }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  const int r = 4 * cus;
+  const int r = 3 * cus;
   if (r > 0 && dev < kMaxDev) cache[dev].store(r, std::memory_order_relaxed);
   return r;
 }

@@ -94,7 +94,7 @@ def test_work_queue_sparse_tickets_and_reuse():
     # The split kernel hands out (sequence, KV head, split) tickets from a work
     # counter. Here a third of the sequences are empty and a third hold under
     # two tiles, so most tickets fall past a sequence's end and the counter
-    # jumps; 48 * 4 * 32 = 6144 tickets for 1024 waves. Two calls on one
+    # jumps; 48 * 4 * 32 = 6144 tickets for 768 waves. Two calls on one
     # workspace (the counter is set by each call), the second with fewer
     # sequences and shorter lengths (rows past the first call's lengths are
     # NaN in these caches).
