@@ -160,8 +160,8 @@ int ssa_decode(const void* q, const void* k_cache, const void* v_cache, const in
                int split_tiles, float lambda, void* workspace, size_t workspace_bytes,
                void* stream);
 
-/* Size of the static device scratch behind ssa_decode_noalloc (16 MiB). */
-#define SSA_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+/* Size of the static device scratch behind ssa_decode_noalloc (32 MiB). */
+#define SSA_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
 
 /*
  * ssa_decode_noalloc -- ssa_decode for callers that cannot allocate device
@@ -174,8 +174,8 @@ int ssa_decode(const void* q, const void* k_cache, const void* v_cache, const in
  * or by any routine it calls.
  *  - Calls whose ssa_decode_workspace_size(...) exceeds
  *    SSA_DECODE_SCRATCH_BYTES return SSA_ERR_SCRATCH and enqueue nothing
- *    (for example B = 32, Hq = 32, S_max = 32768, d = 128, split_tiles = 24
- *    needs 11.7 MB and fits).
+ *    (for example B = 32, Hq = 32, S_max = 32768, d = 128, split_tiles = 16
+ *    needs 17.0 MB and fits).
  *  - All calls on one GPU share that GPU's scratch: calls that overlap on a
  *    GPU (different streams, or host threads without ordering) race. Calls
  *    ordered on one stream are safe. No scratch content needs to start at

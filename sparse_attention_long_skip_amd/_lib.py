@@ -24,7 +24,7 @@ SSA_ERR_UNSUPPORTED = -2
 SSA_ERR_WORKSPACE = -3
 SSA_ERR_HIP = -4
 SSA_ERR_SCRATCH = -5
-DECODE_SCRATCH_BYTES = 16 << 20
+DECODE_SCRATCH_BYTES = 32 << 20
 TILE_KEPT = 1
 TILE_SKIPPED = 2
 

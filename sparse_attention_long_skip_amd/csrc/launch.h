@@ -126,7 +126,7 @@ hipError_t launch_sparge_mask(const SpargeParams& p, hipStream_t stream);
 hipError_t launch_vertical_slash(const VsParams& p, hipStream_t stream);
 // The allocation-free decode entry point's static scratch: its size, and
 // its device address on the current device (looked up once per device).
-constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
 hipError_t decode_scratch(void** ptr);
 hipError_t launch_lambda_for_ratio(const float* margins, long long n, double target, double window,
                                    double* result, void* workspace, hipStream_t stream);

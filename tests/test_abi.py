@@ -117,13 +117,13 @@ def test_decode_noalloc_validation(lib):
     assert _decode_noalloc(lib, lam=1.0) == -1
     assert _decode_noalloc(lib, Hq=12, Hkv=4) == -2
     # partials beyond the static scratch are refused before any HIP call:
-    # B=16, Hq=32, S_max=8192, split 2 tiles -> 64 splits of 130 floats = 17.0 MB
-    need = ssa.decode_workspace_size(16, 32, 8192, 128, 64, 2)
+    # B=32, Hq=32, S_max=8192, split 2 tiles -> 64 splits of 130 floats = 34.1 MB
+    need = ssa.decode_workspace_size(32, 32, 8192, 128, 64, 2)
     assert need > ssa.DECODE_SCRATCH_BYTES
-    assert _decode_noalloc(lib, B=16, Hq=32, Hkv=8, S=8192, T=2) == ssa.SSA_ERR_SCRATCH
+    assert _decode_noalloc(lib, B=32, Hq=32, Hkv=8, S=8192, T=2) == ssa.SSA_ERR_SCRATCH
     assert ssa.status_string(ssa.SSA_ERR_SCRATCH).startswith("SSA_ERR_SCRATCH")
-    # the 32-sequence decode workload fits
-    assert ssa.decode_workspace_size(32, 32, 32768, 128, 64, 24) <= ssa.DECODE_SCRATCH_BYTES
+    # the 32-sequence decode workload (16-tile splits: 17.0 MB) fits
+    assert ssa.decode_workspace_size(32, 32, 32768, 128, 64, 16) <= ssa.DECODE_SCRATCH_BYTES
 
 
 def _mask(lib, **kw):
