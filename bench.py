@@ -262,8 +262,8 @@ def _noop(x):
 
 def _prefill_unit_task(args):
     import oracle
-    unit, lam, Br, Bc, causal = args
-    oracle.prefill(_W["q"], _W["k"], _W["v"], lam, Br, Bc, causal, units=[unit], bits=True)
+    unit, lam, Br, Bc, causal, nm_kw = args
+    oracle.prefill(_W["q"], _W["k"], _W["v"], lam, Br, Bc, causal, units=[unit], bits=True, **nm_kw)
     return unit
 
 
@@ -290,10 +290,29 @@ def _sparse_head_task(args):
     return h, t1 - t0, time.perf_counter() - t1
 
 
+def _masked_head_task(args):
+    """One head: the oracle's mask predictor (SpargeAttn stage one or
+    vertical-slash), then the block-sparse prefill over its lists."""
+    import oracle
+    h, kind, mkw, lam, pool = args
+    q = _W["q"][:, h:h + 1]
+    k = _W["k"][:, h:h + 1]
+    if kind == "sparge":
+        m = oracle.sparge_mask(q, k, pool, mkw["theta"], mkw["tau"], "mass", bits=True)
+    else:
+        m = oracle.vertical_slash_mask(q, k, mkw["last_q"], mkw["n_vertical"], mkw["n_slash"], pool, bits=True)
+    oracle.prefill(q, k, _W["v"][:, h:h + 1], lam, pool, pool, True, block_idx=m["block_idx"],
+                   block_cnt=m["block_cnt"], bits=True)
+    return h
+
+
 def run_cpu_pool(arrays: dict, fn, tasks, budget_s: float):
-    """Run ``fn`` over ``tasks`` in worker processes until the budget is
-    spent. Returns (finished task results, wall seconds, workers)."""
+    """Run ``fn`` over ``tasks`` in worker processes: every worker is kept
+    busy until the budget is spent, then the tasks in flight finish and
+    count (so a task longer than the budget is not lost). Returns (finished
+    task results, wall seconds, workers)."""
     import multiprocessing as mp
+    import queue
     import shutil
     import tempfile
     import numpy as np
@@ -307,38 +326,77 @@ def run_cpu_pool(arrays: dict, fn, tasks, budget_s: float):
         ctx = mp.get_context("spawn")
         with ctx.Pool(nw, initializer=_worker_init, initargs=(paths,)) as pool:
             pool.map(_noop, range(4 * nw))
+            finished = queue.Queue()
+            todo = iter(tasks)
+
+            def submit():
+                t = next(todo, None)
+                if t is None:
+                    return False
+                pool.apply_async(fn, (t,), callback=finished.put, error_callback=finished.put)
+                return True
+
             done = []
             t0 = time.perf_counter()
-            for r in pool.imap_unordered(fn, tasks, chunksize=1):
+            in_flight = sum(1 for _ in range(nw) if submit())
+            while in_flight:
+                r = finished.get()
+                in_flight -= 1
+                if isinstance(r, BaseException):
+                    raise r
                 done.append(r)
-                if time.perf_counter() - t0 > budget_s:
-                    break
+                if time.perf_counter() - t0 <= budget_s and submit():
+                    in_flight += 1
             dt = time.perf_counter() - t0
-            pool.terminate()
         return done, dt, nw
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
 
 
-def cpu_baseline_prefill(cfg_id, lam, budget_s, np, synth, label):
-    """The oracle on the decision units of a prefill workload, in a seeded
-    random order (the whole workload if the budget allows)."""
+def cpu_baseline_prefill(cfg_id, lam, budget_s, np, synth, label, Br=None, nm_kw=None):
+    """The oracle on the decision units (query tiles of Br rows) of a prefill
+    workload, in a seeded random order (the whole workload if the budget
+    allows); ``nm_kw`` adds N:M sparse softmax."""
     c = synth.CONFIGS[cfg_id]
+    Br = Br or c["Br"]
     x = synth.prefill_inputs(cfg_id, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"],
                              frac=c["frac"])
-    nQ = math.ceil(c["L"] / c["Br"])
+    nQ = math.ceil(c["L"] / Br)
     units = [(b, h, i) for b in range(c["B"]) for h in range(c["Hq"]) for i in range(nQ)]
     order = np.random.default_rng(1234).permutation(len(units))
-    tasks = [(units[j], lam, c["Br"], c["Bc"], c["causal"]) for j in order]
+    tasks = [(units[j], lam, Br, c["Bc"], c["causal"], nm_kw or {}) for j in order]
     done, dt, nw = run_cpu_pool({"q": x["q"], "k": x["k"], "v": x["v"]}, _prefill_unit_task, tasks, budget_s)
     flops = 0.0
     for (_, _, i) in done:
-        r0, r1 = i * c["Br"], min(c["L"], (i + 1) * c["Br"])
+        r0, r1 = i * Br, min(c["L"], (i + 1) * Br)
         # dense-equivalent work of these rows: 4 d per allowed (row, key) pair
         flops += 4.0 * c["d"] * (r1 * (r1 + 1) - r0 * (r0 + 1)) / 2
     return {"value": flops / dt / 1e12, "unit": "dense-equiv TFLOP/s", "cores": nw, "kind": "oracle",
-            "sample": f"{len(done)} of {len(units)} query tiles (random order) of the {label} workload, "
-                      f"fp64 numpy, one process per core, {dt:.1f} s"}
+            "sample": f"{len(done)} of {len(units)} {Br}-row query tiles (random order) of the {label} "
+                      f"workload, fp64 numpy, one process per core, {dt:.1f} s"}
+
+
+def cpu_baseline_masked(x, c, kind, mkw, budget_s, label):
+    """The oracle's mask predictor and block-sparse prefill, one task per head."""
+    tasks = [(h, kind, mkw, c["lam"], c["pool"] if "pool" in c else 64) for h in range(c["Hq"])]
+    done, dt, nw = run_cpu_pool({"q": x["q"], "k": x["k"], "v": x["v"]}, _masked_head_task, tasks, budget_s)
+    flops = 4.0 * c["d"] * c["L"] * (c["L"] + 1) / 2 * len(done)
+    return {"value": flops / dt / 1e12, "unit": "dense-equiv TFLOP/s", "cores": nw, "kind": "oracle",
+            "sample": f"{len(done)} of {c['Hq']} heads (mask + block-sparse prefill) of the {label} "
+                      f"workload, fp64 numpy, one process per core, {dt:.1f} s"}
+
+
+def with_cpu(res, args, what, fn):
+    """Attach a CPU baseline to a leg's result unless --no-cpu; an error is
+    reported in place of the figure."""
+    if args.no_cpu:
+        return res
+    log(f"cpu baseline: oracle on {what}")
+    try:
+        res["cpu_baseline"] = fn()
+    except Exception as e:  # report, keep the GPU figures
+        res["cpu_baseline"] = {"error": repr(e)}
+    return res
 
 
 def cpu_baseline_decode(y, c, lam, budget_s, np):
@@ -385,8 +443,12 @@ def extra_128k(args, torch, np, ssa, synth):
                  "mfma_frac_executed": round(ex / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                  "skip_pct": round(100.0 * (vis - kept) / vis, 3)})
     del p
-    return {"workload": "prefill 128K B=1 Hq=8 Hkv=1 d=128 causal Br=128 Bc=64, 5% planted", "sweep": rows,
-            "calibration": cal}
+    torch.cuda.empty_cache()
+    res = {"workload": "prefill 128K B=1 Hq=8 Hkv=1 d=128 causal Br=128 Bc=64, 5% planted", "sweep": rows,
+           "calibration": cal}
+    # the oracle at the first sweep point, on a random sample of the query tiles
+    return with_cpu(res, args, "a sample of the 128K workload",
+                    lambda: cpu_baseline_prefill(3, c["lam_sweep"][0], args.cpu_budget / 2, np, synth, "128K"))
 
 
 def extra_decode(args, torch, np, ssa, synth):
@@ -476,7 +538,6 @@ def extra_sparge(args, torch, np, ssa, synth):
     x = synth.prefill_inputs(c["cfg_id"], 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"],
                              frac=c["frac"], drift=c["drift"])
     q, k, v = (dev_bf16(x[n], torch, np) for n in ("q", "k", "v"))
-    del x
     m = ssa.sparge_mask(q, k, c["theta"], c["tau"], "mass", c["pool"])
     torch.cuda.synchronize()
     cnt = m["block_cnt"]
@@ -488,15 +549,19 @@ def extra_sparge(args, torch, np, ssa, synth):
     ms_mask, ev_mask = time_launches(fm, 10, 3, torch)
     vis, kept, ms_p, ev_p = time_prefill_legs(q, k, v, c["lam"], kw, 10, 3, torch, ssa)
     ex = 2.0 * 64 * 64 * c["d"] * (vis + kept)
-    return {"workload": "SpargeAttn two-stage prefill 32K H=16 d=64, drifting blocks, "
-                        f"theta={c['theta']} tau={c['tau']} (P_hat mass), lambda={c['lam']}",
-            "mask_ms": round(ms_mask, 4),
-            "mask_hbm_gbs": round(2 * 2 * c["Hq"] * c["L"] * c["d"] / (ev_mask * 1e-3) / 1e9, 1),
-            "prefill_ms": round(ms_p, 4), "mask_density": round(vis / n_causal, 4),
-            "in_mask_skip_pct": round(100.0 * (vis - kept) / vis, 3),
-            "combined_sparsity": round(1 - kept / n_causal, 4),
-            "dense_equiv_tflops": round(dense_flops(c) / (ms_mask + ms_p) / 1e9, 1),
-            "mfma_frac_executed": round(ex / (ev_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    res = {"workload": "SpargeAttn two-stage prefill 32K H=16 d=64, drifting blocks, "
+                       f"theta={c['theta']} tau={c['tau']} (P_hat mass), lambda={c['lam']}",
+           "mask_ms": round(ms_mask, 4),
+           "mask_hbm_gbs": round(2 * 2 * c["Hq"] * c["L"] * c["d"] / (ev_mask * 1e-3) / 1e9, 1),
+           "prefill_ms": round(ms_p, 4), "mask_density": round(vis / n_causal, 4),
+           "in_mask_skip_pct": round(100.0 * (vis - kept) / vis, 3),
+           "combined_sparsity": round(1 - kept / n_causal, 4),
+           "dense_equiv_tflops": round(dense_flops(c) / (ms_mask + ms_p) / 1e9, 1),
+           "mfma_frac_executed": round(ex / (ev_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del q, k, v, m
+    return with_cpu(res, args, "the SpargeAttn workload",
+                    lambda: cpu_baseline_masked(x, c, "sparge", {"theta": c["theta"], "tau": c["tau"]},
+                                                args.cpu_budget / 2, "32K SpargeAttn"))
 
 
 def extra_vslash(args, torch, np, ssa, synth):
@@ -506,7 +571,6 @@ def extra_vslash(args, torch, np, ssa, synth):
     c = synth.CONFIGS[4]
     x = synth.prefill_inputs(4, 0, c["B"], c["Hq"], c["Hkv"], c["L"], c["d"], block=c["Bc"], frac=c["frac"])
     q, k, v = (dev_bf16(x[n], torch, np) for n in ("q", "k", "v"))
-    del x
     nv, ns, R = 1000, 64, 64
     m = ssa.vertical_slash_mask(q, k, nv, ns, R)
     torch.cuda.synchronize()
@@ -519,15 +583,19 @@ def extra_vslash(args, torch, np, ssa, synth):
                                      10, 3, torch)
     vis, kept, ms_p, ev_p = time_prefill_legs(q, k, v, c["lam"], kw, 10, 3, torch, ssa)
     ex = 2.0 * 64 * 64 * c["d"] * (vis + kept)
-    return {"workload": f"vertical-slash estimator 32K H=16 d=64 (last {R} queries, {nv} vertical, "
-                        f"{ns} slash) + block-sparse prefill over its tiles, lambda={c['lam']}",
-            "estimator_ms": round(ms_mask, 4),
-            "estimator_k_read_gbs": round(c["Hq"] * c["L"] * c["d"] * 2 / (ev_mask * 1e-3) / 1e9, 1),
-            "prefill_ms": round(ms_p, 4), "mask_density": round(vis / n_causal, 4),
-            "in_mask_skip_pct": round(100.0 * (vis - kept) / vis, 3),
-            "combined_sparsity": round(1 - kept / n_causal, 4),
-            "dense_equiv_tflops": round(dense_flops(c) / (ms_mask + ms_p) / 1e9, 1),
-            "mfma_frac_executed": round(ex / (ev_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    res = {"workload": f"vertical-slash estimator 32K H=16 d=64 (last {R} queries, {nv} vertical, "
+                       f"{ns} slash) + block-sparse prefill over its tiles, lambda={c['lam']}",
+           "estimator_ms": round(ms_mask, 4),
+           "estimator_k_read_gbs": round(c["Hq"] * c["L"] * c["d"] * 2 / (ev_mask * 1e-3) / 1e9, 1),
+           "prefill_ms": round(ms_p, 4), "mask_density": round(vis / n_causal, 4),
+           "in_mask_skip_pct": round(100.0 * (vis - kept) / vis, 3),
+           "combined_sparsity": round(1 - kept / n_causal, 4),
+           "dense_equiv_tflops": round(dense_flops(c) / (ms_mask + ms_p) / 1e9, 1),
+           "mfma_frac_executed": round(ex / (ev_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del q, k, v, m
+    return with_cpu(res, args, "the vertical-slash workload",
+                    lambda: cpu_baseline_masked(x, c, "vslash", {"last_q": R, "n_vertical": nv, "n_slash": ns},
+                                                args.cpu_budget / 2, "32K vertical-slash"))
 
 
 def extra_nm(args, torch, np, ssa, synth):
@@ -546,7 +614,12 @@ def extra_nm(args, torch, np, ssa, synth):
                      "skip_pct": round(100.0 * (vis - kept) / vis, 3),
                      "dense_equiv_tflops": round(dense_flops(c) / ms / 1e9, 1),
                      "mfma_frac_executed": round(2.0 * 128 * 64 * 128 * (vis + kept) / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
-    return {"workload": "N:M 2:4 sparse softmax, 16K GQA shape, dense sink 64 + recent 256 tokens", "runs": rows}
+    del q, k, v
+    res = {"workload": "N:M 2:4 sparse softmax, 16K GQA shape, dense sink 64 + recent 256 tokens", "runs": rows}
+    nm_kw = {"nm": (2, 4), "dense_sink": 64, "dense_recent": 256}
+    return with_cpu(res, args, "the N:M workload",
+                    lambda: cpu_baseline_prefill(1, lam50, args.cpu_budget / 2, np, synth, "16K N:M 2:4",
+                                                 nm_kw=nm_kw))
 
 
 def extra_warp_units(args, torch, np, ssa, synth):
@@ -565,11 +638,14 @@ def extra_warp_units(args, torch, np, ssa, synth):
     vis, kept, ms, ev = time_prefill_legs(q, k, v, lam, kw, 10, 3, torch, ssa)
     wg_vis = visited_tiles_count(c["B"], c["Hq"], c["L"], 128, c["Bc"], True)
     ex = 2.0 * 32 * 64 * c["d"] * (4 * wg_vis + kept)
-    return {"workload": "Br=32 decision units (per-warp skip), 16K GQA shape, lambda calibrated to ~50% unit skip",
-            "lambda": round(lam, 5), "ms": round(ms, 4), "skip_pct": round(100.0 * (vis - kept) / vis, 3),
-            "unit_tiles_visited": vis, "unit_tiles_kept": kept, "workgroup_tiles_visited": wg_vis,
-            "dense_equiv_tflops": round(dense_flops(c) / ms / 1e9, 1),
-            "mfma_frac_executed": round(ex / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del q, k, v
+    res = {"workload": "Br=32 decision units (per-warp skip), 16K GQA shape, lambda calibrated to ~50% unit skip",
+           "lambda": round(lam, 5), "ms": round(ms, 4), "skip_pct": round(100.0 * (vis - kept) / vis, 3),
+           "unit_tiles_visited": vis, "unit_tiles_kept": kept, "workgroup_tiles_visited": wg_vis,
+           "dense_equiv_tflops": round(dense_flops(c) / ms / 1e9, 1),
+           "mfma_frac_executed": round(ex / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    return with_cpu(res, args, "the 32-row-unit workload",
+                    lambda: cpu_baseline_prefill(1, lam, args.cpu_budget / 2, np, synth, "16K", Br=32))
 
 
 def main():
