@@ -126,3 +126,17 @@ def test_work_queue_sparse_tickets_and_reuse():
             nsp = -(-(-(-int(lens_c[b]) // 64)) // 2)
             assert np.all(sc[b, :, nsp:] == 0)
         assert abs(int(sc.sum()) - int(ref["skip_counts"].sum())) <= max(2, int(0.01 * ref["skip_counts"].sum()))
+
+
+def test_work_queue_many_short_sequences():
+    # 256 sequences of 1..700 keys, one-tile splits: 256 * 2 * 11 = 5632
+    # tickets, many times the wave count, so every wave runs a long chain of
+    # splits (including empty ones) from the work counter.
+    rng = np.random.default_rng(307)
+    B, S = 256, 700
+    lens = rng.integers(1, S + 1, B)
+    lens[::17] = 0
+    y = synth.decode_inputs(307, 0, B, 4, 2, S, 64, 1, S, seqlens=lens)
+    for lam in (-math.inf, -0.7):
+        r = decode_parity(y, lam, 1)
+        print(f"lambda={lam}: skipped {r['skipped']}/{r['visited']}")
