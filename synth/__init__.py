@@ -233,10 +233,9 @@ CONFIGS = {
             frac=0.10, lam=-6.0),
     1: dict(kind="prefill", B=1, Hq=32, Hkv=8, L=16384, d=128, Br=128, Bc=64, causal=True,
             frac=0.10, target_skip=0.5),
-    # split_tiles: 16 key tiles per split (about 6300 split waves for these
-    # lengths, three rounds of the 2048 wave slots, the short last splits
-    # dispatched last): 2% faster than 24 tiles and 4% faster than 12 at ~50%
-    # skip with the deferred-P.V kernel
+    # split_tiles: 16 key tiles per split (6368 splits for these lengths):
+    # 2% faster than 24 tiles and 3% faster than 12 at ~50% skip with the
+    # persistent split kernel
     2: dict(kind="decode", B=32, Hq=32, Hkv=8, S_max=32768, d=128, Bc=64, len_lo=16384,
             len_hi=32768, split_tiles=16, frac=0.10, target_skip=0.5),
     3: dict(kind="prefill", B=1, Hq=8, Hkv=1, L=131072, d=128, Br=128, Bc=64, causal=True,

@@ -28,7 +28,7 @@ def test_dense_and_calibrated_small(d, T):
 @pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
 def test_group_sizes(G, d):
-    # every (d, G) instance, including those at one and at two waves per SIMD
+    # every (d, G) instance of the split kernel
     Hkv = 2
     y = synth.decode_inputs(301, G + d, 2, G * Hkv, Hkv, 2048, d, 1500, 2048)
     for lam in (-math.inf, -0.5):
