@@ -359,13 +359,17 @@ void decode_split_kernel(DecodeArgs a) {
 // per batch: lane s holds split s's log-sum-exp lse_s = m_s / sqrt(d) +
 // ln l_s (splits with l_s = 0 hold no kept key and are left out); with
 // top = max lse_s, tot = sum exp(lse_s - top) and out = sum exp(m_s /
-// sqrt(d) - top) o_s / tot, lse = top + ln tot. A lane owns D / 64 output
-// elements; a batch's partial loads are all issued before the first use,
-// and each split's weight reaches every lane by a scalar read.
+// sqrt(d) - top) o_s / tot, lse = top + ln tot. A lane owns D / 64
+// adjacent output elements (one 4- or 8-byte load per partial row); the
+// first U partial rows of a batch are loaded together with the batch's
+// (m, l) pairs, since neither depends on the other, and each split's
+// weight reaches every lane by a scalar read.
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   constexpr int E = D / kWave;  // output elements per lane
   constexpr int U = 32;         // partial rows in flight per lane
+  using Vec = typename std::conditional<E == 2, float2, float>::type;
+  static_assert(E == 1 || E == 2, "head dim 64 or 128");
   const int hq = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
@@ -373,20 +377,23 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   const int ntiles = (n + BC - 1) / BC;
   const int nsp = (ntiles + a.T - 1) / a.T;
   const size_t base = ((size_t)b * a.Hq + hq) * a.nS;
+  const Vec* po = reinterpret_cast<const Vec*>(a.ws_o + base * D) + lane;
+  const float2* pml = reinterpret_cast<const float2*>(a.ws_ml) + base;
   float top = -INFINITY, tot = 0.f;
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   for (int s0 = 0; s0 < nsp; s0 += kWave) {
     const int s = s0 + lane;
+    const int cnt = min(kWave, nsp - s0);
+    const float2 ml = s < nsp ? pml[s] : make_float2(0.f, 0.f);
+    Vec oo[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) oo[u] = u < cnt ? po[(size_t)(s0 + u) * kWave] : Vec{};
     float x = -INFINITY, ms = -INFINITY;
-    if (s < nsp) {
-      const float m = a.ws_ml[(base + s) * 2];
-      const float l = a.ws_ml[(base + s) * 2 + 1];
-      if (l > 0.f) {
-        ms = m * a.inv_sqrt_d;
-        x = ms + __logf(l);
-      }
+    if (ml.y > 0.f) {
+      ms = ml.x * a.inv_sqrt_d;
+      x = ms + __logf(ml.y);
     }
     const float bt = wave_max(x);
     if (bt > top) {
@@ -400,29 +407,32 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
     if (top == -INFINITY) continue;  // no kept key so far
     tot += wave_sum(x == -INFINITY ? 0.f : __expf(x - top));
     const float wo = ms == -INFINITY ? 0.f : __expf(ms - top);
-    const int cnt = min(kWave, nsp - s0);
     for (int u0 = 0; u0 < cnt; u0 += U) {
-      float oo[U][E];
+      if (u0 > 0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-          oo[u][e] = u0 + u < cnt ? a.ws_o[(base + s0 + u0 + u) * D + e * kWave + lane] : 0.f;
+        for (int u = 0; u < U; ++u)
+          oo[u] = u0 + u < cnt ? po[(size_t)(s0 + u0 + u) * kWave] : Vec{};
+      }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const float w = __builtin_amdgcn_readlane(__float_as_int(wo), (u0 + u) & (kWave - 1));
+        const float w = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(wo), (u0 + u) & (kWave - 1)));
+        const float* o = reinterpret_cast<const float*>(&oo[u]);
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = fmaf(__int_as_float(w), oo[u][e], acc[e]);
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(w, o[e], acc[e]);
       }
     }
   }
   const float lse = (tot > 0.f) ? top + __logf(tot) : -INFINITY;
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  uint16_t ob[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const __bf16 rb = (__bf16)(acc[e] * inv);
-    a.out[((size_t)b * a.Hq + hq) * D + e * kWave + lane] = __builtin_bit_cast(uint16_t, rb);
-  }
+  for (int e = 0; e < E; ++e) ob[e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[e] * inv));
+  uint16_t* dst = a.out + ((size_t)b * a.Hq + hq) * D + lane * E;
+  if constexpr (E == 2)
+    *reinterpret_cast<uint32_t*>(dst) = (uint32_t)ob[0] | ((uint32_t)ob[1] << 16);
+  else
+    *dst = ob[0];
   if (a.lse && lane == 0) a.lse[(size_t)b * a.Hq + hq] = lse;
 }
 
