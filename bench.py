@@ -10,7 +10,7 @@ bounded sample of the same workload), and -- under "extra" -- the 128K
 threshold sweep, the decode tokens/s with HBM roofline and the block-sparse
 prefill.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-extra]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 200] [--no-extra]
 """
 
 from __future__ import annotations
@@ -71,13 +71,26 @@ def dev_bf16(bits, torch, np):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def time_launches(fn, steps, warmup, torch):
-    """Warm up, then time `steps` calls: wall clock between synchronisations
-    and HIP events around each call (on the current stream, where the
-    library launches). Returns (ms per step, mean event ms)."""
+# The GPU clock ramps up over the first few hundred milliseconds of load (the
+# 16K prefill launch takes 1.63 ms after 5 warm-up launches, 1.60 after 50 and
+# 1.59 after 200 on one box), so every timed region follows at least this much
+# back-to-back work.
+WARM_S = 0.3
+
+
+def time_launches(fn, steps, warmup, torch, warm_s=WARM_S):
+    """Warm up (`warmup` calls, then further batches of calls until `warm_s`
+    seconds of them have run), then time `steps` calls: wall clock between
+    synchronisations and HIP events around each call (on the current stream,
+    where the library launches). Returns (ms per step, mean event ms)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        for _ in range(max(1, warmup)):
+            fn()
+        torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     t0 = time.perf_counter()
@@ -170,7 +183,7 @@ def time_calibration(p, target, torch, ssa):
             "quantile_ms": round(ms_q, 4), "quantile_event_ms": round(ev_q, 4)}
 
 
-def run_prefill(p, lam, steps, warmup, torch, ssa, check_stats=True):
+def run_prefill(p, lam, steps, warmup, torch, ssa, check_stats=True, warm_s=WARM_S):
     """Time the plain prefill instance (out, lse and per-unit skip counts).
     The kept-tile count comes from the skip counts of the last timed launch;
     with ``check_stats`` a statistics launch (per-tile decisions) beforehand
@@ -182,7 +195,7 @@ def run_prefill(p, lam, steps, warmup, torch, ssa, check_stats=True):
     counts = torch.empty((B, Hq, -(-L // c["Br"])), dtype=torch.int32, device=q.device)
     fn = lambda: ssa.prefill(q, k, v, lam, Br=c["Br"], Bc=c["Bc"], causal=c["causal"], out=out,
                              skip_counts=counts)
-    ms, ev_ms = time_launches(fn, steps, warmup, torch)
+    ms, ev_ms = time_launches(fn, steps, warmup, torch, warm_s)
     vis = visited_tiles_count(B, Hq, L, c["Br"], c["Bc"], c["causal"])
     kept = vis - int(counts.sum().item())
     if check_stats:
@@ -657,7 +670,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="wall seconds per CPU-baseline leg (the oracle in worker processes)")
@@ -693,7 +706,8 @@ def main():
     p = bench_prefill(1, args, torch, np, ssa, synth, target=c["target_skip"])
     lam = p["lam"]
     log(f"lambda {lam:.5f} (calibrated ratio {p['calibrated_ratio']:.4f}); timing {args.steps} steps")
-    vis, kept, ms, ev_ms = run_prefill(p, lam, args.steps, args.warmup, torch, ssa)
+    # exactly args.warmup untimed launches (the default, 200, is ~0.3 s of them)
+    vis, kept, ms, ev_ms = run_prefill(p, lam, args.steps, args.warmup, torch, ssa, warm_s=0.0)
     ex = 2.0 * c["Br"] * c["Bc"] * c["d"] * (vis + kept)
     dense = dense_flops(c)
     value = dense / (ms * 1e-3) / 1e12
