@@ -414,40 +414,67 @@ void prefill_kernel(PrefillArgs a) {
   // of 2 or 4 are lane-local.
   auto nm_sparsify = [&](int kbase) __attribute__((always_inline)) {
     const bool exempt_here = (kbase < a.dense_sink) ||
-        (a.dense_recent > 0 && kbase + BC - 1 > q0 + w * 32 - a.dense_recent);
+        (a.dense_recent > 0 && kbase + BC - 1 > q0 + wu * 32 - a.dense_recent);
+    // e is dropped when at least N members of its group beat it (a higher
+    // score, or an equal score at a lower key). For e < f one comparison
+    // decides the pair: f beats e iff x[f] > x[e], else e beats f (scores
+    // are never NaN). With M = 4, "at least N of e's three possible
+    // beaters" is their OR (N = 1), majority (N = 2) or AND (N = 3), taken
+    // on the comparisons' wave-wide lane masks by the scalar unit.
+    // MODE 1, 2, 3: M = 4 with N = 1, 2, 3; MODE 4: M = 2 with N = 1.
+    auto groups = [&](auto mode_c) __attribute__((always_inline)) {
+      constexpr int MODE = decltype(mode_c)::value;
+      auto atleast = [&](uint64_t p, uint64_t q, uint64_t r) __attribute__((always_inline)) -> uint64_t {
+        if constexpr (MODE == 1) return p | q | r;
+        else if constexpr (MODE == 2) return (p & q) | (r & (p | q));
+        else return p & q & r;
+      };
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        float x[4];
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = s[kb][q4 * 4 + e];
-        // rank of e = members of its group that beat it (higher score, or
-        // equal score and lower key). For e < f one comparison decides the
-        // pair: f beats e iff x[f] > x[e], else e beats f (scores are never
-        // NaN).
-        const bool c01 = x[1] > x[0], c23 = x[3] > x[2];
-        int r0 = c01, r1 = !c01, r2 = c23, r3 = !c23;
-        if (a.nm_m == 4) {
-          const bool c02 = x[2] > x[0], c03 = x[3] > x[0], c12 = x[2] > x[1], c13 = x[3] > x[1];
-          r0 += c02 + c03;
-          r1 += c12 + c13;
-          r2 += !c02 + !c12;
-          r3 += !c03 + !c13;
-        }
-        const bool keep[4] = {r0 < a.nm_n, r1 < a.nm_n, r2 < a.nm_n, r3 < a.nm_n};
-        bool keepx[4] = {keep[0], keep[1], keep[2], keep[3]};
-        if (exempt_here) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = kbase + kb * 32 + q4 * 8 + h * 4 + e;
-            keepx[e] = keepx[e] || key < a.dense_sink || (row - a.dense_recent < key && key <= row);
+          for (int e = 0; e < 4; ++e) x[e] = s[kb][q4 * 4 + e];
+          const uint64_t c01 = __builtin_amdgcn_ballot_w64(x[1] > x[0]);
+          const uint64_t c23 = __builtin_amdgcn_ballot_w64(x[3] > x[2]);
+          uint64_t drop[4];
+          if constexpr (MODE == 4) {
+            drop[0] = c01;
+            drop[1] = ~c01;
+            drop[2] = c23;
+            drop[3] = ~c23;
+          } else {
+            const uint64_t c02 = __builtin_amdgcn_ballot_w64(x[2] > x[0]);
+            const uint64_t c03 = __builtin_amdgcn_ballot_w64(x[3] > x[0]);
+            const uint64_t c12 = __builtin_amdgcn_ballot_w64(x[2] > x[1]);
+            const uint64_t c13 = __builtin_amdgcn_ballot_w64(x[3] > x[1]);
+            drop[0] = atleast(c01, c02, c03);
+            drop[1] = atleast(~c01, c12, c13);
+            drop[2] = atleast(~c02, ~c12, c23);
+            drop[3] = atleast(~c03, ~c13, ~c23);
           }
-        }
+          if (exempt_here) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (!keepx[e]) s[kb][q4 * 4 + e] = -INFINITY;
-      }
+            for (int e = 0; e < 4; ++e) {
+              const int key = kbase + kb * 32 + q4 * 8 + h * 4 + e;
+              drop[e] &= ~__builtin_amdgcn_ballot_w64(key < a.dense_sink ||
+                                                       (row - a.dense_recent < key && key <= row));
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            s[kb][q4 * 4 + e] = __builtin_amdgcn_inverse_ballot_w64(drop[e]) ? -INFINITY : x[e];
+        }
+    };
+    // N >= M keeps every key.
+    if (a.nm_m == 4) {
+      if (a.nm_n == 2) groups(std::integral_constant<int, 2>{});
+      else if (a.nm_n == 1) groups(std::integral_constant<int, 1>{});
+      else if (a.nm_n == 3) groups(std::integral_constant<int, 3>{});
+    } else if (a.nm_n == 1) {
+      groups(std::integral_constant<int, 4>{});
+    }
   };
 
   // tiles (and unit masks) of the current, next and previous positions
