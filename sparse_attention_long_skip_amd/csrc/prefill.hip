@@ -44,6 +44,8 @@
 //  * Workgroups are mapped so that every XCD (own L2) works through whole KV
 //    heads, heaviest causal query tiles first, the G query heads of one KV
 //    head on consecutive slots: the K/V tiles they stream stay L2-resident.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
